@@ -1,0 +1,135 @@
+// The libfattn C ABI: argument validation and dispatch.  Everything here runs
+// on the host and returns before any launch when an argument is rejected.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fattn.h"
+#include "launch.hpp"
+
+namespace fattn {
+namespace {
+
+constexpr long double kMaxElems = 4611686018427387904.0L;   // 2^62
+constexpr long long kMaxRows = 2147483647LL;                // 2^31 - 1
+
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, long double bytes) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Sizes shared by forward and backward.  Returns FA_OK, or the error code.
+// `empty` is set when there is nothing to compute.
+int check_sizes(int B, int H, int Hkv, int N, int d, bool* empty) {
+  *empty = false;
+  if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if ((long double)B * H * N * d > kMaxElems) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N > kMaxRows) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) *empty = true;
+  return FA_OK;
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              int B, int H, int Hkv, int N, int d, float scale, size_t elem, bool* empty) {
+  int st = check_sizes(B, H, Hkv, N, d, empty);
+  if (st != FA_OK || *empty) return st;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  const long double qbytes = (long double)B * H * N * d * elem;
+  const long double kvbytes = (long double)B * Hkv * N * d * elem;
+  const long double lbytes = (long double)B * H * N * 4;
+  const Range rq = range_of(q, qbytes), rk = range_of(k, kvbytes), rv = range_of(v, kvbytes);
+  const Range ro = range_of(o, qbytes), rl = range_of(lse, lbytes);
+  if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv)) return FA_ERR_INVALID_ARG;
+  if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) || overlaps(rl, ro))
+    return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+}  // namespace fattn
+
+using namespace fattn;
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, 2, &empty);
+  if (st != FA_OK || empty) return st;
+  FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream};
+  return status_of(launch_fwd_bf16(a));
+}
+
+extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int H, int Hkv, int N, int d, int causal, float scale,
+                          hipStream_t stream) {
+  bool empty = false;
+  int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, 4, &empty);
+  if (st != FA_OK || empty) return st;
+  FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale, stream};
+  return status_of(launch_fwd_f32(a));
+}
+
+extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  bool empty = false;
+  if (check_sizes(B, H, Hkv, N, d, &empty) != FA_OK || empty) return 0;
+  // D_i = dO_i . O_i per query row, fp32, rounded up to 256 bytes.
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                      void* workspace, int B, int H, int Hkv, int N, int d, int causal,
+                      float scale, hipStream_t stream) {
+  bool empty = false;
+  int st = check_sizes(B, H, Hkv, N, d, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  const void* p16[] = {q, k, v, o, dO, dq, dk, dv, workspace};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  if (!aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const long double qb = (long double)B * H * N * d * 2;
+  const long double kvb = (long double)B * Hkv * N * d * 2;
+  const long double lb = (long double)B * H * N * 4;
+  const Range in[] = {range_of(q, qb), range_of(k, kvb), range_of(v, kvb),
+                      range_of(o, qb), range_of(lse, lb), range_of(dO, qb)};
+  const Range out[] = {range_of(dq, qb), range_of(dk, kvb), range_of(dv, kvb),
+                       range_of(workspace, (long double)fa_bwd_workspace_bytes(B, H, Hkv, N, d))};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : in)
+      if (overlaps(out[i], r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return FA_ERR_INVALID_ARG;
+  }
+  BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace),
+            B, H, Hkv, N, d, causal != 0, scale, stream};
+  return status_of(launch_bwd_bf16(a));
+}
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    default: return "unknown libfattn status";
+  }
+}

@@ -1,0 +1,61 @@
+// Internal launcher declarations (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace fattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, N, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: D_i = dO_i . O_i, fp32 [B, H, N]
+  int B, H, Hkv, N, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_f32(const FwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
+
+// Launch a kernel and return the runtime's verdict on exactly this launch.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                         hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+  std::tuple<KArgs...> held(std::forward<Args>(args)...);
+  return std::apply(
+      [&](auto&... x) {
+        void* argv[] = {static_cast<void*>(&x)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, shmem,
+                               stream);
+      },
+      held);
+}
+
+}  // namespace fattn

@@ -1,0 +1,113 @@
+/*
+ * libfattn -- exact tiled (Flash) attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For every batch b, query head h and query row i:
+ *
+ *     s_ij   = scale * q[b,h,i,:] . k[b,g,j,:]      g = h / (H / Hkv)
+ *     visible(i,j) = !causal || j <= i
+ *     O[b,h,i,:] = sum_j softmax_j(s_i.)[visible] * v[b,g,j,:]
+ *     LSE[b,h,i] = ln sum_{visible j} exp(s_ij)
+ *
+ * This is attention written out as score, softmax and weighted average
+ * ("LLM Architecture Refresh [3]: Flash Attention Is Exact", section 1; the
+ * stable softmax of section 2; the causal mask of section 5).  The forward
+ * computes it tile by tile with a running max, running sum and unnormalised
+ * output per query row, rescaled whenever a later tile raises the max ("How
+ * FlashAttention Uses Tiling", "The Running Statistics"; the same page 3,
+ * section 4), skips key tiles that lie wholly in the future of a causal
+ * query tile (section 7), and never writes the N x N score matrix to memory.
+ * The backward recomputes the probabilities from Q, K, V and the saved LSE
+ * (section 8) instead of storing them.
+ *
+ * Layout (all tensors dense and row-major, no strides):
+ *     q, o, dO, dq      [B, H,   N, d]
+ *     k, v, dk, dv      [B, Hkv, N, d]
+ *     lse               [B, H,   N]      float32, natural log, scaled-score units
+ * Query head h reads key/value head h / (H / Hkv); H must be a multiple of
+ * Hkv.  Causal masking is square: key j is visible to query i iff j <= i.
+ *
+ * Ownership and execution.  Every pointer is a device pointer owned by the
+ * caller.  The library allocates nothing, never synchronises, and enqueues
+ * its kernels on `stream` (NULL = the default stream) in order; a call returns
+ * as soon as the work is enqueued.  Faults during execution surface at the
+ * caller's next synchronisation.  All calls are thread-safe (no global state).
+ *
+ * Errors.  Arguments are validated before anything is launched; on a non-zero
+ * return nothing was enqueued and no output was touched:
+ *     FA_ERR_INVALID_ARG  null pointer, negative size, H, Hkv or d <= 0,
+ *                         H % Hkv != 0, non-finite scale, a pointer not aligned
+ *                         to 16 bytes (4 for lse), an output overlapping an
+ *                         input, or sizes whose index space exceeds 2^62;
+ *     FA_ERR_UNSUPPORTED  a head dimension other than 64 or 128;
+ *     FA_ERR_HIP          the HIP runtime refused the launch.
+ * B == 0 or N == 0 is an empty problem: FA_OK, nothing is read, written or
+ * launched, and the pointers may be NULL.
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,
+    FA_ERR_UNSUPPORTED = -2,
+    FA_ERR_HIP = -3
+};
+
+/*
+ * Forward, bf16 storage.  q, k, v, o are bf16 (IEEE binary16-brain, raw
+ * 16-bit patterns); products accumulate in fp32 on the matrix cores; the
+ * running max/sum/rescale are fp32; o is rounded to bf16 with
+ * round-to-nearest-even; lse is fp32.  d must be 64 or 128.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/*
+ * Forward, fp32 storage and fp32 arithmetic throughout (the variant for
+ * single-precision inputs; same operation, layout and errors as fa_fwd).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (the per-row
+ * D_i = dO_i . O_i terms, fp32).  Returns 0 for an empty problem and for
+ * invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+/*
+ * Backward with recomputation, bf16 storage.  Inputs q, k, v, o (the output
+ * of fa_fwd), lse (from fa_fwd) and dO; outputs dq [B,H,N,d], dk and dv
+ * [B,Hkv,N,d], all bf16 except lse.  The gradient of sum(O * dO):
+ *     P_ij  = exp(s_ij - LSE_i)            dV_j = sum_i P_ij dO_i
+ *     dS_ij = P_ij (dO_i.v_j - dO_i.O_i)   dQ_i = scale sum_j dS_ij k_j
+ *                                          dK_j = scale sum_i dS_ij q_i
+ * with dK, dV of a key/value head summed over the query heads that read it.
+ * `workspace` is caller-owned device memory of at least
+ * fa_bwd_workspace_bytes(...) bytes, 16-byte aligned; its contents on entry
+ * are ignored.  The result is deterministic (no atomics).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, void* dq, void* dk, void* dv, void* workspace,
+           int B, int H, int Hkv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

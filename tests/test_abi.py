@@ -1,0 +1,126 @@
+"""The C ABI: the library loads, exports every function include/fattn.h
+declares, and rejects bad arguments before any launch.  CPU only: every call
+here returns from argument validation (or is a pure host query), so no GPU
+and no HIP work is involved."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fattn.h")
+
+
+def _lib():
+    import exact_tiled_attention_31_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_tiled_attention_31_amd import _build
+        _build.build()
+    return fa, fa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_calls():
+    assert declared_functions() == sorted(
+        ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    fa, lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(fa.PROTOTYPES)
+
+
+def test_status_strings():
+    fa, lib = _lib()
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        s = fa.fa_status_string(code)
+        assert s.startswith("FA_")
+    assert "unknown" in fa.fa_status_string(12345)
+
+
+def test_workspace_bytes():
+    fa, lib = _lib()
+    assert fa.fa_bwd_workspace_bytes(2, 16, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 3, 1, 5, 64) == 256         # rounded up to 256
+    assert fa.fa_bwd_workspace_bytes(0, 16, 16, 4096, 128) == 0     # empty
+    assert fa.fa_bwd_workspace_bytes(1, 16, 3, 4096, 128) == 0      # invalid
+    assert fa.fa_bwd_workspace_bytes(1, 16, 16, 4096, 96) == 0      # unsupported d
+
+
+# Fake, never-dereferenced addresses: validation rejects before any launch.
+A = 1 << 40
+P = [ctypes.c_void_p(A + i * (1 << 32)) for i in range(12)]
+
+
+def fwd(lib, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=4, Hkv=2, N=128, d=128,
+        causal=1, scale=0.1, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_forward_validation(f32):
+    fa, lib = _lib()
+    INV, UNS = fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED
+    for kw in ({"q": None}, {"k": None}, {"v": None}, {"o": None}, {"lse": None},
+               {"H": 0}, {"Hkv": 0}, {"d": 0}, {"B": -1}, {"N": -1}, {"H": 6, "Hkv": 4},
+               {"scale": float("nan")}, {"scale": float("inf")},
+               {"q": ctypes.c_void_p(A + 8)}, {"lse": ctypes.c_void_p(A + (5 << 32) + 2)},
+               {"o": P[0]}, {"o": ctypes.c_void_p(A + 1024)},          # o overlaps q
+               {"lse": P[3]}, {"lse": P[1]},                            # lse overlaps o / k
+               {"B": 1 << 20, "H": 1 << 12, "N": 1 << 12}):             # rows exceed 2^31-1
+        assert fwd(lib, f32=f32, **kw) == INV, kw
+    for d in (32, 96, 256):
+        assert fwd(lib, f32=f32, d=d) == UNS, d
+    # empty problems are a no-op and may pass NULL pointers
+    for kw in ({"B": 0}, {"N": 0}):
+        assert fwd(lib, f32=f32, q=None, k=None, v=None, o=None, lse=None, **kw) == fa.FA_OK
+
+
+def test_backward_validation():
+    fa, lib = _lib()
+
+    def bwd(**kw):
+        args = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7],
+                    dv=P[8], ws=P[9], B=1, H=4, Hkv=2, N=128, d=128, causal=1, scale=0.1)
+        args.update(kw)
+        a = args
+        return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                          a["dv"], a["ws"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                          a["causal"], a["scale"], None)
+
+    INV = fa.FA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert bwd(**{name: None}) == INV, name
+    for kw in ({"dq": P[0]}, {"dk": P[1]}, {"dv": P[5]}, {"ws": P[6]}, {"dk": P[8]},
+               {"dq": ctypes.c_void_p(A + (6 << 32) + 4)}, {"H": 5, "Hkv": 2},
+               {"scale": float("nan")}):
+        assert bwd(**kw) == INV, kw
+    assert bwd(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(N=0, q=None, dq=None) == fa.FA_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    fa, lib = _lib()
+    q = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(q, q, q)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "exact_tiled_attention_31_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "oracle/" not in text, f
