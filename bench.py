@@ -1,0 +1,185 @@
+"""Benchmark: exact tiled attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload (the headline configuration): B=1, 32 query heads on 8 key/value
+heads, N=8192, d=128, bf16 storage, causal, scale 1/sqrt(128); Q, K, V iid
+N(0,1) from seed 3 with 1% of key rows per kv head scaled x8.  Inputs are
+generated on the host, copied to HBM once, and are resident before timing.
+
+A step is one fa_fwd call over the whole batch.  W untimed warm-up steps,
+then K steps bracketed by device synchronisation on both sides.  Prints one
+JSON line:
+  value     causal-adjusted TFLOP/s = 4*B*H*N^2*d/2 / (wall time per step)
+  roofline  the forward kernel against the dense bf16 matrix-core peak; its
+            duration comes from HIP events recorded on the launch stream
+  cpu_baseline  the float64 oracle on a bounded sample of the same inputs
+            (a few query heads, full rows), timed on the host cores.
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
+FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_31_amd", "csrc", f)
+               for f in ("fwd_bf16.hip", "common.hpp")]
+
+
+def fwd_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in FWD_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != fwd_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, heads: int):
+    """Time the float64 oracle on `heads` query heads of the same inputs."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"), default=1)
+    except Exception:   # threadpoolctl absent: report the affinity set
+        blas_threads = len(os.sched_getaffinity(0))
+    heads = max(1, min(heads, w.H))
+    sel = [int(h) for h in np.linspace(0, w.H - 1, heads).round()]
+    t0 = time.perf_counter()
+    for h in sel:
+        g = oracle.kv_head_of(h, w.H, w.Hkv)
+        oracle.attention_fwd(inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1],
+                             w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.B * len(sel) * w.N * w.N * w.d / (2.0 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"float64 numpy oracle on {len(sel)} of {w.H} query heads (all "
+                      f"{w.N} rows, causal prefix), same seeded inputs; "
+                      f"{len(os.sched_getaffinity(0))} host cores visible, "
+                      f"BLAS threads {blas_threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="query heads the oracle baseline computes (bounded sample)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
+                                   "the forward shards over (batch, kv-head) groups without "
+                                   "any exchange, so there is no multi-GPU path to measure"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_31_amd as fa
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fa.lib()
+    dev = torch.device("cuda:0")
+    w = W.C3
+    inp = W.gen_inputs(w)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(inp.q_bits), to_dev(inp.k_bits), to_dev(inp.v_bits)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.causal_adjusted_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    out = {
+        "metric": "attention fwd TFLOP/s (causal-adjusted) at N=8192 d=128 bf16; % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GQA causal forward B=1 H=32 Hkv=8 N=8192 d=128 bf16, "
+                               "1% of K rows x8 (seed 3)",
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": True,
+                   "flops_per_step": flops, "flop_convention": "4*B*H*N^2*d/2"},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
