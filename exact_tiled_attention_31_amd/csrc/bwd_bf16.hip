@@ -1,7 +1,436 @@
-// Backward with recomputation (bf16): placeholder until the kernels land.
+// Backward pass with recomputation, bf16 storage, bf16 matrix cores with
+// fp32 accumulation (gfx950).
+//
+// The probabilities are not stored by the forward; they are recomputed tile
+// by tile from Q, K and the saved log-sum-exp ("LLM Architecture Refresh
+// [3]: Flash Attention Is Exact", section 8, the paragraph on the backward
+// pass).  With P_ij = exp(s_ij - LSE_i) on visible pairs and dP_ij = dO_i.v_j,
+// the gradient of sum(O * dO) is
+//     D_i  = sum_j P_ij dP_ij  (= dO_i . O_i for the exact O)
+//     dS_ij = P_ij (dP_ij - D_i)
+//     dV_j = sum_i P_ij dO_i,   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
+//
+// Three kernels, no atomics (deterministic):
+//   1. rows<DELTA>: one workgroup per (batch, query head, 128-query block),
+//      lane = query; walks the visible key tiles computing S^T = K Q^T and
+//      dP^T = V dO^T and sums D_i = sum_j P_ij dP_ij in fp32.  D is taken
+//      from the recomputed P and dP rather than from the bf16-rounded O, whose
+//      rounding would otherwise dominate the gradient error.
+//   2. dk_dv: one workgroup per (batch, kv head, 128-key block); each wave
+//      owns 32 keys (lane = key) with its K and V rows in registers and fp32
+//      dK^T, dV^T accumulators; it walks every query head of the group and
+//      every 64-query tile that sees the block: S = Q K^T, P, dP = dO V^T,
+//      dS, dV^T += dO^T P, dK^T += Q^T dS.  Q and dO are staged in LDS
+//      row-major and transposed.
+//   3. rows<GRAD>: as 1, then dS^T and dQ^T += K^T dS^T.
+// P and dS enter the matrix cores as hi + lo bf16 pairs (two steps against
+// the same exact bf16 operand), so their rounding stays near fp32.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fattn {
-hipError_t launch_bwd_bf16(const BwdArgs&) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Query-block stationary kernel: D (DELTA) or dQ (GRAD)
+// ---------------------------------------------------------------------------
+constexpr int kQB = 128;   // queries per workgroup (4 waves x 32)
+constexpr int kKT = 64;    // keys per tile
+
+enum RowMode { kDelta = 0, kGrad = 1 };
+
+template <int D>
+struct QTile {
+  static constexpr int kRowStride = D + 8;
+  static constexpr int kTStride = kKT + 8;
+  static constexpr int kKSteps = D / 16;
+  static constexpr int kDBlocks = D / 32;
+  static constexpr int kBlocks = (kKT / 4) * (D / 8);
+  static_assert(kBlocks <= kThreads, "one block per thread at most");
+};
+
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void rows_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, float* __restrict__ delta,
+    uint16_t* __restrict__ dQ, int B, int H, int Hkv, int N, float c, float scale,
+    int n_qblocks) {
+  using T = QTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kKT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[MODE == kGrad ? D * T::kTStride : 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int grp = lane >> 5;
+
+  const int BH = B * H;
+  const int item_q = blockIdx.x / BH;
+  const int bh = blockIdx.x - item_q * BH;
+  const int qb = CAUSAL ? (n_qblocks - 1 - item_q) : item_q;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int g = h / (H / Hkv);
+  const int q0 = qb * kQB;
+  const size_t head_q = (size_t)bh * N;
+  const size_t head_kv = ((size_t)b * Hkv + g) * N;
+
+  const int qi = q0 + 32 * wave + col;
+  const bool qok = qi < N;
+  u32x4_t qf[T::kKSteps], of[T::kKSteps];
+  {
+    const uint16_t* qr = Q + (head_q + (qok ? qi : 0)) * D + 8 * grp;
+    const uint16_t* dr = dO + (head_q + (qok ? qi : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < T::kKSteps; ++s) {
+      qf[s] = qok ? *reinterpret_cast<const u32x4_t*>(qr + 16 * s) : u32x4_t{0, 0, 0, 0};
+      of[s] = qok ? *reinterpret_cast<const u32x4_t*>(dr + 16 * s) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  const float l2 = qok ? LSE[head_q + qi] * kLog2e : 0.f;
+  const float dd = (MODE == kGrad && qok) ? delta[head_q + qi] : 0.f;
+
+  float dsum = 0.f;   // DELTA: this lane's share of sum_j P_ij dP_ij
+  f32x16_t dq[T::kDBlocks];
+#pragma unroll
+  for (int cb = 0; cb < T::kDBlocks; ++cb) dq[cb] = f32x16_t{};
+
+  const int q_hi = min(q0 + kQB, N);
+  int n_kt = (N + kKT - 1) / kKT;
+  if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kKT + 1);
+  const int wq_first = q0 + 32 * wave;
+  const int wq_last = wq_first + 31;
+  const int blk_r = (tid / (D / 8)) * 4;
+  const int blk_c = (tid % (D / 8)) * 8;
+  const bool loader = tid < T::kBlocks;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kKT;
+    __syncthreads();
+    if (loader) {
+      u32x4_t kr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = k0 + blk_r + r;
+        const bool ok = kj < N;
+        kr[r] = ok ? *reinterpret_cast<const u32x4_t*>(K + (head_kv + kj) * D + blk_c)
+                   : u32x4_t{0, 0, 0, 0};
+        const u32x4_t vr = ok ? *reinterpret_cast<const u32x4_t*>(V + (head_kv + kj) * D + blk_c)
+                              : u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(&sK[(blk_r + r) * T::kRowStride + blk_c]) = kr[r];
+        *reinterpret_cast<u32x4_t*>(&sV[(blk_r + r) * T::kRowStride + blk_c]) = vr;
+      }
+      if (MODE == kGrad) store_block_transposed(sKt, T::kTStride, blk_c, blk_r, kr);
+    }
+    __syncthreads();
+
+    if (wq_first >= N) continue;
+    if (CAUSAL && k0 > wq_last) continue;
+    const bool need_mask = (k0 + kKT > N) || (CAUSAL && k0 + kKT - 1 > wq_first) || !qok;
+
+    // S^T = K Q^T, dP^T = V dO^T : two 32-key blocks, lane = query, regs = keys
+    f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t p_acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int s = 0; s < T::kKSteps; ++s) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = (32 * kb + col) * T::kRowStride + 16 * s + 8 * grp;
+        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(&sK[off]);
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&sV[off]);
+        s_acc[kb] = mfma_32x32x16_bf16(ak, qf[s], s_acc[kb]);
+        p_acc[kb] = mfma_32x32x16_bf16(av, of[s], p_acc[kb]);
+      }
+    }
+
+    u32x4_t ds_hi[2][2], ds_lo[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = fast_exp2(fmaf(s_acc[kb][r], c, -l2));
+        if (need_mask) {
+          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * grp + (r & 3);
+          const bool dead = !qok || (kj >= N) || (CAUSAL && kj > qi);
+          if (dead) pv = 0.f;
+        }
+        if (MODE == kDelta) dsum = fmaf(pv, p_acc[kb][r], dsum);
+        else ds[r] = pv * (p_acc[kb][r] - dd);
+      }
+      if (MODE == kGrad) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) split_bf16x8(&ds[8 * t], ds_hi[kb][t], ds_lo[kb][t]);
+      }
+    }
+
+    if (MODE == kGrad) {
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int cb = 0; cb < T::kDBlocks; ++cb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                &sKt[(32 * cb + col) * T::kTStride + 32 * kb + 16 * t + 8 * grp]);
+            dq[cb] = mfma_32x32x16_bf16(a, ds_hi[kb][t], dq[cb]);
+            dq[cb] = mfma_32x32x16_bf16(a, ds_lo[kb][t], dq[cb]);
+          }
+        }
+      }
+    }
+  }
+
+  if (MODE == kDelta) {
+    const float total = dsum + swap_half(dsum);
+    if (qok && grp == 0) delta[head_q + qi] = total;
+  } else if (qok) {
+    uint16_t* row = dQ + (head_q + qi) * D;
+#pragma unroll
+    for (int cb = 0; cb < T::kDBlocks; ++cb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * cb + 8 * r4 + 4 * grp;
+        u32x2_t w;
+        w.x = pack_bf16x2(dq[cb][4 * r4 + 0] * scale, dq[cb][4 * r4 + 1] * scale);
+        w.y = pack_bf16x2(dq[cb][4 * r4 + 2] * scale, dq[cb][4 * r4 + 3] * scale);
+        *reinterpret_cast<u32x2_t*>(row + d0) = w;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-block stationary
+// ---------------------------------------------------------------------------
+constexpr int kKB = 128;   // keys per workgroup (4 waves x 32)
+constexpr int kQT = 64;    // queries per tile
+
+template <int D>
+struct KVTile {
+  static constexpr int kRowStride = D + 8;     // row-major Q / dO tile (bf16 elements)
+  static constexpr int kTStride = kQT + 8;     // transposed Q^T / dO^T tile
+  static constexpr int kKSteps = D / 16;
+  static constexpr int kDBlocks = D / 32;
+  static constexpr int kBlocks = (kQT / 4) * (D / 8);   // 4-row x 8-col blocks per tile
+  static_assert(kBlocks <= kThreads, "one block per thread at most");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    int B, int H, int Hkv, int N, float c, float scale) {
+  using T = KVTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kQT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * T::kTStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[kQT * T::kRowStride];   // dO row-major
+  __shared__ __attribute__((aligned(16))) uint16_t sOt[D * T::kTStride];      // dO^T
+  __shared__ __attribute__((aligned(16))) float sL[kQT];                       // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[kQT];                       // D_i
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int grp = lane >> 5;
+
+  const int BG = B * Hkv;
+  const int kb = blockIdx.x / BG;     // heavy (early) key blocks first
+  const int bg = blockIdx.x - kb * BG;
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
+  const int k0 = kb * kKB;
+  const int kw0 = k0 + 32 * wave;     // this wave's first key
+  const int key = kw0 + col;          // this lane's key
+  const int rep = H / Hkv;
+
+  const size_t head_kv = ((size_t)b * Hkv + g) * N;
+  // K and V rows of this lane's key (B operands over d)
+  u32x4_t kf[T::kKSteps], vf[T::kKSteps];
+  {
+    const bool ok = key < N;
+    const uint16_t* kr = K + (head_kv + (ok ? key : 0)) * D + 8 * grp;
+    const uint16_t* vr = V + (head_kv + (ok ? key : 0)) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < T::kKSteps; ++s) {
+      kf[s] = ok ? *reinterpret_cast<const u32x4_t*>(kr + 16 * s) : u32x4_t{0, 0, 0, 0};
+      vf[s] = ok ? *reinterpret_cast<const u32x4_t*>(vr + 16 * s) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+
+  f32x16_t dk[T::kDBlocks], dv[T::kDBlocks];
+#pragma unroll
+  for (int cb = 0; cb < T::kDBlocks; ++cb) {
+    dk[cb] = f32x16_t{};
+    dv[cb] = f32x16_t{};
+  }
+
+  const int qt_first = CAUSAL ? (k0 / kQT) : 0;
+  const int n_qt = (N + kQT - 1) / kQT;
+  const int blk_r = (tid / (D / 8)) * 4;    // loader: 4 rows x 8 columns per thread
+  const int blk_c = (tid % (D / 8)) * 8;
+  const bool loader = tid < T::kBlocks;
+
+  for (int hh = 0; hh < rep; ++hh) {
+    const int h = g * rep + hh;
+    const size_t head_q = ((size_t)b * H + h) * N;
+    for (int qt = qt_first; qt < n_qt; ++qt) {
+      const int q0 = qt * kQT;
+      __syncthreads();   // previous tile fully consumed
+      if (loader) {
+        u32x4_t qr[4], orow[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = q0 + blk_r + r;
+          const bool ok = qi < N;
+          qr[r] = ok ? *reinterpret_cast<const u32x4_t*>(Q + (head_q + qi) * D + blk_c)
+                     : u32x4_t{0, 0, 0, 0};
+          orow[r] = ok ? *reinterpret_cast<const u32x4_t*>(dO + (head_q + qi) * D + blk_c)
+                       : u32x4_t{0, 0, 0, 0};
+          *reinterpret_cast<u32x4_t*>(&sQ[(blk_r + r) * T::kRowStride + blk_c]) = qr[r];
+          *reinterpret_cast<u32x4_t*>(&sO[(blk_r + r) * T::kRowStride + blk_c]) = orow[r];
+        }
+        store_block_transposed(sQt, T::kTStride, blk_c, blk_r, qr);
+        store_block_transposed(sOt, T::kTStride, blk_c, blk_r, orow);
+      }
+      if (tid < kQT) {
+        const int qi = q0 + tid;
+        sL[tid] = qi < N ? LSE[head_q + qi] * kLog2e : 0.f;
+        sD[tid] = qi < N ? delta[head_q + qi] : 0.f;
+      }
+      __syncthreads();
+
+      // this wave's keys kw0..kw0+31 against queries q0..q0+63
+      if (kw0 >= N) continue;
+      if (CAUSAL && q0 + kQT - 1 < kw0) continue;   // every query precedes every key
+      const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31);
+
+      // S = Q K^T, dP = dO V^T : two 32-query blocks, lane = key, regs = queries
+      f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
+      f32x16_t p_acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+      for (int s = 0; s < T::kKSteps; ++s) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int off = (32 * qb + col) * T::kRowStride + 16 * s + 8 * grp;
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQ[off]);
+          const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sO[off]);
+          s_acc[qb] = mfma_32x32x16_bf16(aq, kf[s], s_acc[qb]);
+          p_acc[qb] = mfma_32x32x16_bf16(ao, vf[s], p_acc[qb]);
+        }
+      }
+
+      u32x4_t p_hi[2][2], p_lo[2][2], ds_hi[2][2], ds_lo[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float p[16], ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qq = 32 * qb + 8 * r4 + 4 * grp;    // 4 consecutive query rows
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[qq]);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[qq]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float pv = fast_exp2(fmaf(s_acc[qb][r], c, -l4[e]));
+            if (need_mask) {
+              const int qi = q0 + qq + e;
+              const bool dead = (qi >= N) || (key >= N) || (CAUSAL && key > qi);
+              if (dead) pv = 0.f;
+            }
+            p[r] = pv;
+            ds[r] = pv * (p_acc[qb][r] - d4[e]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          split_bf16x8(&p[8 * t], p_hi[qb][t], p_lo[qb][t]);
+          split_bf16x8(&ds[8 * t], ds_hi[qb][t], ds_lo[qb][t]);
+        }
+      }
+
+      // dV^T += dO^T P, dK^T += Q^T dS : lane = key, regs = d
+#pragma unroll
+      for (int cb = 0; cb < T::kDBlocks; ++cb) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int off = (32 * cb + col) * T::kTStride + 32 * qb + 16 * t + 8 * grp;
+            const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sOt[off]);
+            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQt[off]);
+            dv[cb] = mfma_32x32x16_bf16(ao, p_hi[qb][t], dv[cb]);
+            dv[cb] = mfma_32x32x16_bf16(ao, p_lo[qb][t], dv[cb]);
+            dk[cb] = mfma_32x32x16_bf16(aq, ds_hi[qb][t], dk[cb]);
+            dk[cb] = mfma_32x32x16_bf16(aq, ds_lo[qb][t], dk[cb]);
+          }
+        }
+      }
+    }
+  }
+
+  if (key < N) {
+    uint16_t* dkr = dK + (head_kv + key) * D;
+    uint16_t* dvr = dV + (head_kv + key) * D;
+#pragma unroll
+    for (int cb = 0; cb < T::kDBlocks; ++cb) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * cb + 8 * r4 + 4 * grp;
+        u32x2_t wk, wv;
+        wk.x = pack_bf16x2(dk[cb][4 * r4 + 0] * scale, dk[cb][4 * r4 + 1] * scale);
+        wk.y = pack_bf16x2(dk[cb][4 * r4 + 2] * scale, dk[cb][4 * r4 + 3] * scale);
+        wv.x = pack_bf16x2(dv[cb][4 * r4 + 0], dv[cb][4 * r4 + 1]);
+        wv.y = pack_bf16x2(dv[cb][4 * r4 + 2], dv[cb][4 * r4 + 3]);
+        *reinterpret_cast<u32x2_t*>(dkr + d0) = wk;
+        *reinterpret_cast<u32x2_t*>(dvr + d0) = wv;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_all(const BwdArgs& a) {
+  const float c = a.scale * kLog2e;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
+  const int n_qb = (a.N + kQB - 1) / kQB;
+  const dim3 row_grid((unsigned)((long long)n_qb * a.B * a.H));
+
+  hipError_t e = launch_kernel(rows_kernel<D, CAUSAL, kDelta>, row_grid, dim3(kThreads), 0,
+                               a.stream, q, k, v, dO, a.lse, a.delta,
+                               static_cast<uint16_t*>(nullptr), a.B, a.H, a.Hkv, a.N, c, a.scale,
+                               n_qb);
+  if (e != hipSuccess) return e;
+
+  const int n_kb = (a.N + kKB - 1) / kKB;
+  e = launch_kernel(dk_dv_kernel<D, CAUSAL>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(kThreads),
+                    0, a.stream, q, k, v, dO, a.lse, static_cast<const float*>(a.delta),
+                    static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.B, a.H, a.Hkv,
+                    a.N, c, a.scale);
+  if (e != hipSuccess) return e;
+
+  return launch_kernel(rows_kernel<D, CAUSAL, kGrad>, row_grid, dim3(kThreads), 0, a.stream, q, k,
+                       v, dO, a.lse, a.delta, static_cast<uint16_t*>(a.dq), a.B, a.H, a.Hkv, a.N,
+                       c, a.scale, n_qb);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_all<128, true>(a) : launch_all<128, false>(a);
+  return a.causal ? launch_all<64, true>(a) : launch_all<64, false>(a);
+}
+
 }  // namespace fattn

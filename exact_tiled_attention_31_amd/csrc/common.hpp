@@ -40,8 +40,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight fp32 values as bf16 (RNE) in one 16-byte operand.
+__device__ __forceinline__ u32x4_t pack_bf16x8(const float* x) {
+  return u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                 pack_bf16x2(x[6], x[7])};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight fp32 values as a pair of bf16 operands hi + lo, hi = bf16(x) and
+// lo = bf16(x - hi): the sum carries about 16 significant bits, so a product
+// against an exact bf16 operand split over two matrix-core steps keeps
+// near-fp32 accuracy.
+__device__ __forceinline__ void split_bf16x8(const float* x, u32x4_t& hi, u32x4_t& lo) {
+  hi = pack_bf16x8(x);
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = x[2 * i] - bf16_lo(hi[i]);
+    r[2 * i + 1] = x[2 * i + 1] - bf16_hi(hi[i]);
+  }
+  lo = pack_bf16x8(r);
+}
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -62,6 +83,36 @@ __device__ __forceinline__ uint32_t pack_lo_halves(uint32_t a, uint32_t b) {
 // High 16-bit halves of two words: {hi16(b) : hi16(a)}.
 __device__ __forceinline__ uint32_t pack_hi_halves(uint32_t a, uint32_t b) {
   return byte_perm(b, a, 0x07060302u);
+}
+
+// Position of row kk inside a transposed (d-major) LDS tile: bits 2 and 3
+// swapped.  Register r of a 32x32 accumulator holds row 8*(r/4) + 4*grp +
+// r%4 of its block; after the swap the 8 rows one lane feeds to one operand
+// (registers 8t..8t+7) sit at 8 consecutive positions 16t + 8*grp + 0..7, so
+// the matching transposed operand is a single 16-byte LDS read.
+__device__ __forceinline__ int tr_pos(int kk) {
+  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// Store a 4-row x 8-column bf16 block (rows r0..r0+3, given as four 16-byte
+// row segments) transposed into a d-major LDS tile: column c goes to
+// dst[(c0 + c) * stride + tr_pos(r0) .. +3].  r0 must be a multiple of 4.
+__device__ __forceinline__ void store_block_transposed(uint16_t* dst, int stride, int c0, int r0,
+                                                       const u32x4_t (&rows)[4]) {
+  const int pos0 = tr_pos(r0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int w = i >> 1;
+    u32x2_t pair;
+    if ((i & 1) == 0) {
+      pair.x = pack_lo_halves(rows[0][w], rows[1][w]);
+      pair.y = pack_lo_halves(rows[2][w], rows[3][w]);
+    } else {
+      pair.x = pack_hi_halves(rows[0][w], rows[1][w]);
+      pair.y = pack_hi_halves(rows[2][w], rows[3][w]);
+    }
+    *reinterpret_cast<u32x2_t*>(&dst[(c0 + i) * stride + pos0]) = pair;
+  }
 }
 
 }  // namespace fattn

@@ -81,19 +81,26 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes (the per-row
- * D_i = dO_i . O_i terms, fp32).  Returns 0 for an empty problem and for
- * invalid sizes.
+ * D_i = sum_j P_ij dP_ij terms, fp32 [B, H, N], rounded up to 256 bytes).
+ * Returns 0 for an empty problem and for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 /*
- * Backward with recomputation, bf16 storage.  Inputs q, k, v, o (the output
- * of fa_fwd), lse (from fa_fwd) and dO; outputs dq [B,H,N,d], dk and dv
- * [B,Hkv,N,d], all bf16 except lse.  The gradient of sum(O * dO):
- *     P_ij  = exp(s_ij - LSE_i)            dV_j = sum_i P_ij dO_i
- *     dS_ij = P_ij (dO_i.v_j - dO_i.O_i)   dQ_i = scale sum_j dS_ij k_j
- *                                          dK_j = scale sum_i dS_ij q_i
+ * Backward with recomputation ("LLM Architecture Refresh [3]: Flash
+ * Attention Is Exact", section 8: the probabilities are recomputed from Q, K,
+ * V and the saved statistics rather than stored), bf16 storage.  Inputs q, k,
+ * v, o (the output of fa_fwd), lse (from fa_fwd) and dO; outputs dq
+ * [B,H,N,d], dk and dv [B,Hkv,N,d], all bf16 except lse.  The gradient of
+ * sum(O * dO):
+ *     P_ij  = exp(s_ij - LSE_i)           dP_ij = dO_i . v_j
+ *     D_i   = sum_j P_ij dP_ij            dS_ij = P_ij (dP_ij - D_i)
+ *     dV_j  = sum_i P_ij dO_i             dQ_i  = scale sum_j dS_ij k_j
+ *                                         dK_j  = scale sum_i dS_ij q_i
  * with dK, dV of a key/value head summed over the query heads that read it.
+ * D_i equals dO_i . O_i for the exact output; it is recomputed in fp32 from
+ * P and dP because the bf16-rounded o would dominate the gradient error, so
+ * `o` is validated (non-null, aligned, no overlap with outputs) but not read.
  * `workspace` is caller-owned device memory of at least
  * fa_bwd_workspace_bytes(...) bytes, 16-byte aligned; its contents on entry
  * are ignored.  The result is deterministic (no atomics).
