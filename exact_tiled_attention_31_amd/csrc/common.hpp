@@ -23,6 +23,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -72,6 +76,18 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of x over the lane pair (l, l ^ 32), on the VALU (v_permlane32_swap):
+// the swap returns {x with the lower half copied up, x with the upper half
+// copied down}, so combining the two is symmetric in the pair.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Byte select: result byte i = byte sel[i] of the 8-byte value {hi:lo}.
 __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -113,6 +129,60 @@ __device__ __forceinline__ void store_block_transposed(uint16_t* dst, int stride
     }
     *reinterpret_cast<u32x2_t*>(&dst[(c0 + i) * stride + pos0]) = pair;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Buffer unit: global -> LDS copies and range-checked addressing
+// ---------------------------------------------------------------------------
+
+// LLVM's raw buffer load into LDS: each lane copies `size` bytes from
+// rsrc.base + voffset + soffset + offset to LDS at lds + 16 * lane (lds is
+// wave-uniform).  Offsets at or past rsrc.num_records read as zero.
+extern "C" __device__ void fattn_llvm_raw_buffer_load_lds(i32x4_t rsrc, lds_u32_t* lds, int size,
+                                                          int voffset, int soffset, int offset,
+                                                          int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor for `bytes` bytes at `base` (stride 0, raw addressing).
+__device__ __forceinline__ i32x4_t make_buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = (int32_t)(uint32_t)(a & 0xffffffffu);
+  r[1] = (int32_t)(uint32_t)((a >> 32) & 0xffffu);
+  r[2] = (int32_t)bytes;
+  r[3] = 0x00020000;   // gfx9 data format word: raw dword access
+  return r;
+}
+
+// Copy 16 bytes per lane from the buffer at `voffset` into LDS at
+// `lds_wave_dst + 16 * lane` (`lds_wave_dst` must be wave-uniform).
+__device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, void* lds_wave_dst, int voffset) {
+  fattn_llvm_raw_buffer_load_lds(rsrc, (lds_u32_t*)lds_wave_dst, 16, voffset, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// buffer -> LDS copies) number at most N.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// During the prologue two tiles are in flight; wait for the first only.
+template <int kOpsPerTile>
+__device__ __forceinline__ void wait_vmem_at_most_one_tile(bool second_in_flight) {
+  if (second_in_flight) wait_vmem_at_most<kOpsPerTile>();
+  else wait_vmem_all();
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q supplies the
+// address of 4 consecutive 16-bit elements; lane g receives element g%4 of
+// the chunks supplied by lanes g/4, 4 + g/4, 8 + g/4, 12 + g/4 (in that order).
+// With lane 4j+q pointing at row r0+j, columns c0+4q.., lane g gets column
+// c0+g of rows r0..r0+3.
+__device__ __forceinline__ u32x2_t ds_read_tr16_b64(const void* lds_addr) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds_addr);
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 }  // namespace fattn
