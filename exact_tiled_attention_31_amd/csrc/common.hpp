@@ -168,11 +168,27 @@ __device__ __forceinline__ void wait_vmem_at_most() {
 }
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// During the prologue two tiles are in flight; wait for the first only.
-template <int kOpsPerTile>
-__device__ __forceinline__ void wait_vmem_at_most_one_tile(bool second_in_flight) {
-  if (second_in_flight) wait_vmem_at_most<kOpsPerTile>();
-  else wait_vmem_all();
+// Wait until at most n (wave-uniform, 0..15) vector-memory operations are
+// outstanding.
+__device__ __forceinline__ void wait_vmem_leq(int n) {
+  switch (n) {
+    case 0: wait_vmem_at_most<0>(); break;
+    case 1: wait_vmem_at_most<1>(); break;
+    case 2: wait_vmem_at_most<2>(); break;
+    case 3: wait_vmem_at_most<3>(); break;
+    case 4: wait_vmem_at_most<4>(); break;
+    case 5: wait_vmem_at_most<5>(); break;
+    case 6: wait_vmem_at_most<6>(); break;
+    case 7: wait_vmem_at_most<7>(); break;
+    case 8: wait_vmem_at_most<8>(); break;
+    case 9: wait_vmem_at_most<9>(); break;
+    case 10: wait_vmem_at_most<10>(); break;
+    case 11: wait_vmem_at_most<11>(); break;
+    case 12: wait_vmem_at_most<12>(); break;
+    case 13: wait_vmem_at_most<13>(); break;
+    case 14: wait_vmem_at_most<14>(); break;
+    default: wait_vmem_at_most<15>(); break;
+  }
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q supplies the

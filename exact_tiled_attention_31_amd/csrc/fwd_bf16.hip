@@ -19,18 +19,19 @@
 //     (buffer_load_dwordx4 ... lds, 16 bytes per lane, no VGPR staging);
 //     rows past N read as zero.  Tiles are double-buffered with one barrier
 //     per tile; the copy of tile j+2 is in flight while tile j+1 waits;
-//   * LDS rows are unpadded; each 16-byte chunk is XOR-swizzled by its row so
-//     that the K reads (ds_read_b128, 16 consecutive rows) and the V
-//     transpose reads (ds_read_b64_tr_b16, 8 rows x 64 bytes) are free of
-//     bank conflicts;
+//   * LDS rows are padded (K by 16 bytes, V by 32) so that the K reads
+//     (ds_read_b128, 16 consecutive rows) and the V transpose reads
+//     (ds_read_b64_tr_b16, 8 rows x 64 bytes) avoid bank conflicts while every
+//     read address stays one base register plus an immediate; the copy points
+//     pad slots past the end of the buffer;
 //   * the scores are computed transposed, S^T = K Q^T, so each lane owns one
 //     query row: the row max needs one exchange with the other half-wave
 //     (v_permlane32_swap) and the score accumulator becomes the P^T operand of
 //     O^T += V^T P^T without leaving registers.  V^T operands come straight
 //     from row-major V through the transpose read;
 //   * the halves are staggered: S of half 1 runs on the matrix cores while
-//     half 0 does its softmax, and half 1's softmax overlaps half 0's P.V;
-//     V fragments are read once per tile and reused by both halves;
+//     half 0 does its softmax; K and V fragments are read once per tile and
+//     used by both halves;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA; the
 //     scale is never applied to Q in bf16;
 //   * heavy causal query blocks are dispatched first.
@@ -46,35 +47,30 @@ constexpr int kBM = kWaves * kQW;     // query rows per workgroup
 constexpr int kBN = 64;               // keys per tile
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -__builtin_inff();
+// How far (log2 units) a row max may exceed the running reference before the
+// accumulator is rebased: terms up to 2^24 keep every fp32 sum far from
+// overflow for any realistic |V| and N.
+constexpr float kSlack = 24.f;
 
 template <int D>
 struct Tile {
-  static constexpr int kRowBytes = 2 * D;                // unpadded bf16 row
+  static constexpr int kRowBytes = 2 * D;                // one bf16 row in global memory
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  static constexpr int kRowsPer256 = 256 / kRowBytes;    // rows sharing one 256-byte bank span
-  static constexpr int kTileBytes = kBN * kRowBytes;
-  static constexpr int kSlots = kTileBytes / 16;         // 16-byte copy slots per tile
-  static constexpr int kCopiesPerThread = kSlots / kThreads;
+  // LDS rows are padded by one 16-byte slot (K) or two (V): K rows then start
+  // 4 banks apart (16 consecutive rows read with ds_read_b128 hit distinct
+  // banks), V rows 8 banks apart (the 8-row transpose reads pair up evenly).
+  static constexpr int kKSlots = kChunks + 1;            // 16-byte slots per K row in LDS
+  static constexpr int kVSlots = kChunks + 2;            // ... per V row
+  static constexpr int kKStride = 16 * kKSlots;          // bytes
+  static constexpr int kVStride = 16 * kVSlots;
+  static constexpr int kKTile = kBN * kKStride;
+  static constexpr int kVTile = kBN * kVStride;
+  static constexpr int kKCopies = kBN * kKSlots / 64;    // wave-wide copy instructions per K tile
+  static constexpr int kVCopies = kBN * kVSlots / 64;
   static constexpr int kKSteps = D / 16;                 // contraction steps of S^T over d
   static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
-  static_assert(kSlots % kThreads == 0, "tile copy split");
+  static_assert((kBN * kKSlots) % 64 == 0 && (kBN * kVSlots) % 64 == 0, "whole copy instructions");
 };
-
-// XOR swizzle of the 16-byte chunk index within an LDS row.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  using T = Tile<D>;
-  constexpr int kQ = T::kChunks / 4;
-  const int m = row / T::kRowsPer256;
-  return 4 * (m % kQ) + (m / kQ) % 4;
-}
-
-// Byte offset in a tile of element (row, col) (col a multiple of 4).
-template <int D>
-__device__ __forceinline__ int lds_off(int row, int col) {
-  using T = Tile<D>;
-  return row * T::kRowBytes + 16 * ((col >> 3) ^ swz<D>(row)) + 2 * (col & 7);
-}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
@@ -82,8 +78,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks) {
   using T = Tile<D>;
-  // [buffer][K | V] tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * T::kTileBytes];
+  // [buffer][K tile | V tile]
+  constexpr int kStage = T::kKTile + T::kVTile;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+  // per-wave scratch for the rare rebase of the output accumulator
+  __shared__ __attribute__((aligned(16))) float rescale_scratch[kWaves * 64 * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -132,26 +131,38 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   int n_kt = (N + kBN - 1) / kBN;
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kBN + 1);
 
-  // ---- tile copy: slot = (instruction, wave, lane) -> (row, swizzled chunk) --
-  int copy_src[T::kCopiesPerThread];   // byte offset of this lane's chunk within a tile's rows
-#pragma unroll
-  for (int i = 0; i < T::kCopiesPerThread; ++i) {
-    const int slot = (i * kWaves + wave) * 64 + lane;
-    const int row = slot / T::kChunks;
-    const int pchunk = slot % T::kChunks;
-    copy_src[i] = row * T::kRowBytes + 16 * (pchunk ^ swz<D>(row));
-  }
+  // ---- tile copy: wave-wide instruction j fills LDS slots 64j .. 64j+63 ------
+  // (lane order).  Slot -> (row, chunk) of the padded layout; pad slots and rows
+  // past N are pointed past the end of the buffer and read as zero.
+  const uint32_t kv_bytes = (uint32_t)N * T::kRowBytes;
+  auto copy_offset = [&](int slot, int slots_per_row) {
+    const int row = slot / slots_per_row;
+    const int chunk = slot - row * slots_per_row;
+    return chunk < T::kChunks ? row * T::kRowBytes + 16 * chunk : -1;
+  };
   auto issue_tile = [&](int k0, int buf) {
-    uint8_t* kdst = smem + (2 * buf) * T::kTileBytes;
-    uint8_t* vdst = kdst + T::kTileBytes;
+    uint8_t* kdst = smem + buf * kStage;
+    uint8_t* vdst = kdst + T::kKTile;
     const int base = k0 * T::kRowBytes;
 #pragma unroll
-    for (int i = 0; i < T::kCopiesPerThread; ++i) {
-      const int wslot = (i * kWaves + wave) * 64 * 16;   // this wave's 1 KB destination
-      buffer_load_lds16(k_rsrc, kdst + wslot, base + copy_src[i]);
-      buffer_load_lds16(v_rsrc, vdst + wslot, base + copy_src[i]);
+    for (int j0 = 0; j0 < T::kKCopies; j0 += kWaves) {
+      const int j = j0 + wave;
+      if (j < T::kKCopies) {
+        const int off = copy_offset(64 * j + lane, T::kKSlots);
+        buffer_load_lds16(k_rsrc, kdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
+      }
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < T::kVCopies; j0 += kWaves) {
+      const int j = j0 + wave;
+      if (j < T::kVCopies) {
+        const int off = copy_offset(64 * j + lane, T::kVSlots);
+        buffer_load_lds16(v_rsrc, vdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
+      }
     }
   };
+  // copy instructions of one tile issued by this wave
+  const int my_copies = (T::kKCopies - wave + kWaves - 1) / kWaves + (T::kVCopies - wave + kWaves - 1) / kWaves;
 
   // ---- running state (log2 units), per half ---------------------------------
   float m2[2] = {kNegInf, kNegInf};
@@ -171,16 +182,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            kt_lds + lds_off<D>(32 * kb + col, 16 * s + 8 * grp));
+            kt_lds + (32 * kb + col) * T::kKStride + 32 * s + 16 * grp);
         sacc[kb] = mfma_32x32x16_bf16(a, qf[hf][s], sacc[kb]);
       }
     }
   };
 
-  // softmax of one half's 32 x 64 score tile -> bf16 P^T operands; updates m, l, O
+  // softmax of one half's 32 x 64 score tile -> bf16 P^T operands; updates l.
+  // The running reference m (log2 units) is raised lazily: exp2(s*c - m) may
+  // exceed 1 by up to 2^kSlack before m is moved, so the accumulator is
+  // rebased only when some row's max outgrows m by more than kSlack.  O and l
+  // always share m, so the result is the same; fp32 holds the larger terms.
+  // c > 0 always (the host clamps it), so masked scores of -inf give
+  // exp2(-inf) = 0 without a select.
   auto softmax_half = [&](f32x16_t (&sacc)[2], int hf, int k0, bool need_mask,
                           u32x4_t (&pf)[2][2]) {
     if (need_mask) {
+      asm volatile("" ::: "memory");   // a real branch: unmasked tiles pay nothing
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -196,106 +214,108 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
-    smax = pair_max(smax);
-    const float mx = (smax == kNegInf) ? kNegInf : smax * c;
-    const float m_new = fmaxf(m2[hf], mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float corr = fast_exp2(m2[hf] - m_use);   // 0 while nothing was seen
+    if (__builtin_expect(__any(smax * c > m2[hf] + kSlack), 0)) {
+      // raise the reference to the row max and rebase what is held
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m2[hf], pair_max(smax) * c);
+      // 0 while nothing was seen; 1 for a row that is still entirely masked
+      const float corr = (m_new == kNegInf) ? 1.f : fast_exp2(m2[hf] - m_new);
+      l[hf] *= corr;
+      // The accumulator lives in AGPRs, which the VALU cannot read; it goes
+      // through LDS (which moves AGPR data directly) to be scaled, so that no
+      // VALU use of it exists and it never has to be held in VGPRs.
+      volatile f32x4_t* scr = reinterpret_cast<volatile f32x4_t*>(rescale_scratch) + wave * 64 * 4 + lane;
+#pragma unroll
+      for (int cb = 0; cb < T::kDBlocks; ++cb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4_t x = {oacc[hf][cb][4 * q4], oacc[hf][cb][4 * q4 + 1], oacc[hf][cb][4 * q4 + 2],
+                       oacc[hf][cb][4 * q4 + 3]};
+          scr[64 * q4] = x;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4_t x = scr[64 * q4];
+          x *= corr;
+          scr[64 * q4] = x;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t x = scr[64 * q4];
+          oacc[hf][cb][4 * q4] = x[0];
+          oacc[hf][cb][4 * q4 + 1] = x[1];
+          oacc[hf][cb][4 * q4 + 2] = x[2];
+          oacc[hf][cb][4 * q4 + 3] = x[3];
+        }
+      }
+      m2[hf] = m_new;
+    }
+    const float m_use = (m2[hf] == kNegInf) ? 0.f : m2[hf];
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = fast_exp2(fmaf(sacc[kb][r], c, -m_use));
-        if (need_mask && sacc[kb][r] == kNegInf) e = 0.f;   // exact zero even if c == 0
-        p[r] = e;
-        psum += e;
+        p[r] = fast_exp2(fmaf(sacc[kb][r], c, -m_use));
+        psum += p[r];
       }
       pf[kb][0] = pack_bf16x8(&p[0]);
       pf[kb][1] = pack_bf16x8(&p[8]);
     }
-    l[hf] = l[hf] * corr + psum;
-    if (__any(corr != 1.f)) {
-#pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[hf][cb][r] *= corr;
-    }
-    m2[hf] = m_new;
+    l[hf] += psum;
   };
 
   // V^T operand (32 d x 16 keys) for d-block cb, key block kb, step t:
   // two transpose reads of 4 keys each (keys 16t + 4*grp + 0..3 and +8).
-  const int tr_j = (lane & 15) >> 2;                 // row within the 4-row group
-  const int tr_col = 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+  const int tr_base = (4 * grp + ((lane & 15) >> 2)) * T::kVStride +
+                      2 * (4 * (lane & 3) + 16 * ((lane >> 4) & 1));
   auto v_operand = [&](const uint8_t* vt_lds, int cb, int kb, int t) {
-    const int key = 32 * kb + 16 * t + 4 * grp + tr_j;
-    const int dcol = 32 * cb + tr_col;
-    const u32x2_t lo = ds_read_tr16_b64(vt_lds + lds_off<D>(key, dcol));
-    const u32x2_t hi = ds_read_tr16_b64(vt_lds + lds_off<D>(key + 8, dcol));
+    const uint8_t* p = vt_lds + tr_base + (32 * kb + 16 * t) * T::kVStride + 64 * cb;
+    const u32x2_t lo = ds_read_tr16_b64(p);
+    const u32x2_t hi = ds_read_tr16_b64(p + 8 * T::kVStride);
     return u32x4_t{lo.x, lo.y, hi.x, hi.y};
   };
 
   // ---- main loop: one barrier per tile, LDS double-buffered ----------------
   issue_tile(0, 0);
-  if (n_kt > 1) issue_tile(kBN, 1);
-  wait_vmem_at_most_one_tile<2 * T::kCopiesPerThread>(n_kt > 1);
+  if (n_kt > 1) {
+    issue_tile(kBN, 1);
+    wait_vmem_leq(my_copies);   // tile 0's copies (issued first) have landed
+  } else {
+    wait_vmem_all();
+  }
   __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const int k0 = kt * kBN;
-    const uint8_t* kt_lds = smem + (2 * buf) * T::kTileBytes;
-    const uint8_t* vt_lds = kt_lds + T::kTileBytes;
+    const uint8_t* kt_lds = smem + buf * kStage;
+    const uint8_t* vt_lds = kt_lds + T::kKTile;
 
     const bool act0 = (wq_first < N) && !(CAUSAL && k0 > wq_first + 31);
     const bool act1 = (wq_first + 32 < N) && !(CAUSAL && k0 > wq_first + 63);
-    if (act1) {   // act0 implies act1 unless the second half is past N
+    if (act0 || act1) {
       f32x16_t s0[2], s1[2];
       u32x4_t pf0[2][2], pf1[2][2];
-      u32x4_t vf[T::kDBlocks][2][2];
       const bool mask0 = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > wq_first);
       const bool mask1 = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > wq_first + 32);
+      // half 0's softmax can run while half 1's scores are on the matrix cores
       if (act0) scores(kt_lds, 0, s0);
-      scores(kt_lds, 1, s1);
+      if (act1) scores(kt_lds, 1, s1);
       if (act0) softmax_half(s0, 0, k0, mask0, pf0);
+      if (act1) softmax_half(s1, 1, k0, mask1, pf1);
+      // O^T += V^T P^T; each V operand is read once and used by both halves
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) vf[cb][kb][t] = v_operand(vt_lds, cb, kb, t);
-      if (act0) {
-#pragma unroll
-        for (int cb = 0; cb < T::kDBlocks; ++cb)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              oacc[0][cb] = mfma_32x32x16_bf16(vf[cb][kb][t], pf0[kb][t], oacc[0][cb]);
-      }
-      softmax_half(s1, 1, k0, mask1, pf1);
-#pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[1][cb] = mfma_32x32x16_bf16(vf[cb][kb][t], pf1[kb][t], oacc[1][cb]);
-    } else if (act0) {   // only the first half is below N
-      f32x16_t s0[2];
-      u32x4_t pf0[2][2];
-      const bool mask0 = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > wq_first);
-      scores(kt_lds, 0, s0);
-      softmax_half(s0, 0, k0, mask0, pf0);
-#pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[0][cb] = mfma_32x32x16_bf16(v_operand(vt_lds, cb, kb, t), pf0[kb][t], oacc[0][cb]);
+          for (int t = 0; t < 2; ++t) {
+            const u32x4_t a = v_operand(vt_lds, cb, kb, t);
+            if (act0) oacc[0][cb] = mfma_32x32x16_bf16(a, pf0[kb][t], oacc[0][cb]);
+            if (act1) oacc[1][cb] = mfma_32x32x16_bf16(a, pf1[kb][t], oacc[1][cb]);
+          }
     }
 
     // tile kt+1 must have landed and every wave must be done with buffer `buf`
@@ -331,7 +351,9 @@ template <int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a) {
   const int n_qblocks = (a.N + kBM - 1) / kBM;
   const long long items = (long long)n_qblocks * a.B * a.H;
-  const float c = fabsf(a.scale) * kLog2e;
+  // c > 0 lets masked scores (-inf) give exp2(-inf) = 0 directly; for scale 0
+  // a c of 1e-30 changes no weight (|s| c stays far below fp32 resolution).
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg_q = a.scale < 0.f ? 1 : 0;
   return launch_kernel(fwd_bf16_kernel<D, CAUSAL>, dim3((unsigned)items), dim3(kThreads), 0,
                        a.stream, static_cast<const uint16_t*>(a.q),
