@@ -5,16 +5,19 @@
 // "Tiled attention in 40 lines", with section 2's running statistics and
 // section 7's causal tile skipping; "How FlashAttention Uses Tiling", update
 // equations under "The Running Statistics"): for one query block, stream the
-// key/value tiles through on-chip memory; per tile compute the scores, raise
-// the running max m, rebase the running sum l and the unnormalised output by
-// exp(m_old - m_new), add the tile's exp(s - m_new) and p.V, and divide by l
-// once at the end.  Tiles whose first key lies after the block's last query
-// are never loaded.  The N x N scores never leave registers.
+// key/value tiles through on-chip memory; per tile compute the scores, keep a
+// running reference m per row, rebase the running sum l and the unnormalised
+// output by exp(m_old - m_new) whenever m moves, add the tile's
+// exp(s - m) and p.V, and divide by l once at the end.  Tiles whose first key
+// lies after the block's last query are never loaded.  The N x N scores
+// never leave registers.
 //
 // Mapping onto CDNA4:
-//   * one workgroup = 4 waves = 256 query rows; each wave owns 64 rows as two
-//     32-row halves and keeps their Q fragments, fp32 output accumulators and
-//     m, l in registers;
+//   * a workgroup of W waves owns W*R query rows (R = 32 or 64 rows per wave,
+//     held as R/32 blocks of 32); each wave keeps its Q fragments, fp32 output
+//     accumulators (AGPRs) and m, l in registers.  With R = 32 two waves share
+//     each SIMD, so one wave's softmax and LDS waits overlap the other's
+//     matrix-core work;
 //   * 64-key tiles of K and V are copied global -> LDS by the buffer unit
 //     (buffer_load_dwordx4 ... lds, 16 bytes per lane, no VGPR staging);
 //     rows past N read as zero.  Tiles are double-buffered with one barrier
@@ -25,13 +28,11 @@
 //     read address stays one base register plus an immediate; the copy points
 //     pad slots past the end of the buffer;
 //   * the scores are computed transposed, S^T = K Q^T, so each lane owns one
-//     query row: the row max needs one exchange with the other half-wave
-//     (v_permlane32_swap) and the score accumulator becomes the P^T operand of
+//     query row and the score accumulator becomes the P^T operand of
 //     O^T += V^T P^T without leaving registers.  V^T operands come straight
 //     from row-major V through the transpose read;
-//   * the halves are staggered: S of half 1 runs on the matrix cores while
-//     half 0 does its softmax; K and V fragments are read once per tile and
-//     used by both halves;
+//   * the running reference is raised lazily (see softmax_block), so the
+//     common path has no cross-lane reduction and never touches O;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA; the
 //     scale is never applied to Q in bf16;
 //   * heavy causal query blocks are dispatched first.
@@ -41,11 +42,7 @@
 namespace fattn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQW = 64;               // query rows per wave (two 32-row halves)
-constexpr int kBM = kWaves * kQW;     // query rows per workgroup
-constexpr int kBN = 64;               // keys per tile
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = 64;   // keys per tile
 constexpr float kNegInf = -__builtin_inff();
 // How far (log2 units) a row max may exceed the running reference before the
 // accumulator is rebased: terms up to 2^24 keep every fp32 sum far from
@@ -72,17 +69,19 @@ struct Tile {
   static_assert((kBN * kKSlots) % 64 == 0 && (kBN * kVSlots) % 64 == 0, "whole copy instructions");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
+template <int D, bool CAUSAL, int WAVES, int BLOCKS>
+__global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks) {
   using T = Tile<D>;
+  constexpr int kRowsPerWave = 32 * BLOCKS;
+  constexpr int kBM = WAVES * kRowsPerWave;
   // [buffer][K tile | V tile]
   constexpr int kStage = T::kKTile + T::kVTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
   // per-wave scratch for the rare rebase of the output accumulator
-  __shared__ __attribute__((aligned(16))) float rescale_scratch[kWaves * 64 * 16];
+  __shared__ __attribute__((aligned(16))) float rescale_scratch[WAVES * 64 * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,17 +105,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   const i32x4_t k_rsrc = make_buffer_rsrc(K + head_kv * D, (uint32_t)N * T::kRowBytes);
   const i32x4_t v_rsrc = make_buffer_rsrc(V + head_kv * D, (uint32_t)N * T::kRowBytes);
 
-  const int wq_first = q0 + wave * kQW;   // this wave's first query row
-  int qi[2];
-  qi[0] = wq_first + col;
-  qi[1] = wq_first + 32 + col;
+  const int wq_first = q0 + wave * kRowsPerWave;   // this wave's first query row
+  int qi[BLOCKS];
+#pragma unroll
+  for (int hf = 0; hf < BLOCKS; ++hf) qi[hf] = wq_first + 32 * hf + col;
 
-  // ---- Q fragments (B operands of S^T), one set per half --------------------
-  u32x4_t qf[2][T::kKSteps];
+  // ---- Q fragments (B operands of S^T), one set per 32-row block ------------
+  u32x4_t qf[BLOCKS][T::kKSteps];
   {
     const uint32_t flip = neg_q ? 0x80008000u : 0u;   // exact sign flip for scale < 0
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < BLOCKS; ++hf) {
       const bool ok = qi[hf] < N;
       const uint16_t* qrow = Qh + (size_t)(ok ? qi[hf] : 0) * D + 8 * grp;
 #pragma unroll
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     uint8_t* vdst = kdst + T::kKTile;
     const int base = k0 * T::kRowBytes;
 #pragma unroll
-    for (int j0 = 0; j0 < T::kKCopies; j0 += kWaves) {
+    for (int j0 = 0; j0 < T::kKCopies; j0 += WAVES) {
       const int j = j0 + wave;
       if (j < T::kKCopies) {
         const int off = copy_offset(64 * j + lane, T::kKSlots);
@@ -153,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       }
     }
 #pragma unroll
-    for (int j0 = 0; j0 < T::kVCopies; j0 += kWaves) {
+    for (int j0 = 0; j0 < T::kVCopies; j0 += WAVES) {
       const int j = j0 + wave;
       if (j < T::kVCopies) {
         const int off = copy_offset(64 * j + lane, T::kVSlots);
@@ -162,18 +161,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
   };
   // copy instructions of one tile issued by this wave
-  const int my_copies = (T::kKCopies - wave + kWaves - 1) / kWaves + (T::kVCopies - wave + kWaves - 1) / kWaves;
+  const int my_copies = (T::kKCopies - wave + WAVES - 1) / WAVES + (T::kVCopies - wave + WAVES - 1) / WAVES;
 
-  // ---- running state (log2 units), per half ---------------------------------
-  float m2[2] = {kNegInf, kNegInf};
-  float l[2] = {0.f, 0.f};   // partial: this lane's keys only; lane pairs are summed at the end
-  f32x16_t oacc[2][T::kDBlocks];
+  // ---- running state (log2 units), per 32-row block -------------------------
+  float m2[BLOCKS], l[BLOCKS];   // l: this lane's keys only; lane pairs are summed at the end
+  f32x16_t oacc[BLOCKS][T::kDBlocks];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int hf = 0; hf < BLOCKS; ++hf) {
+    m2[hf] = kNegInf;
+    l[hf] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] = f32x16_t{};
+  }
 
-  // S^T = K Q^T for one half (32 keys x 32 queries per block, two key blocks)
+  // S^T = K Q^T for one block (32 keys x 32 queries per accumulator, two key blocks)
   auto scores = [&](const uint8_t* kt_lds, int hf, f32x16_t (&sacc)[2]) {
     sacc[0] = f32x16_t{};
     sacc[1] = f32x16_t{};
@@ -188,15 +189,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
   };
 
-  // softmax of one half's 32 x 64 score tile -> bf16 P^T operands; updates l.
+  // softmax of one block's 32 x 64 score tile -> bf16 P^T operands; updates l.
   // The running reference m (log2 units) is raised lazily: exp2(s*c - m) may
   // exceed 1 by up to 2^kSlack before m is moved, so the accumulator is
   // rebased only when some row's max outgrows m by more than kSlack.  O and l
   // always share m, so the result is the same; fp32 holds the larger terms.
   // c > 0 always (the host clamps it), so masked scores of -inf give
   // exp2(-inf) = 0 without a select.
-  auto softmax_half = [&](f32x16_t (&sacc)[2], int hf, int k0, bool need_mask,
-                          u32x4_t (&pf)[2][2]) {
+  auto softmax_block = [&](f32x16_t (&sacc)[2], int hf, int k0, bool need_mask,
+                           u32x4_t (&pf)[2][2]) {
     if (need_mask) {
       asm volatile("" ::: "memory");   // a real branch: unmasked tiles pay nothing
 #pragma unroll
@@ -224,7 +225,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       // The accumulator lives in AGPRs, which the VALU cannot read; it goes
       // through LDS (which moves AGPR data directly) to be scaled, so that no
       // VALU use of it exists and it never has to be held in VGPRs.
-      volatile f32x4_t* scr = reinterpret_cast<volatile f32x4_t*>(rescale_scratch) + wave * 64 * 4 + lane;
+      volatile f32x4_t* scr =
+          reinterpret_cast<volatile f32x4_t*>(rescale_scratch) + wave * 64 * 4 + lane;
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb) {
 #pragma unroll
@@ -293,19 +295,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const uint8_t* kt_lds = smem + buf * kStage;
     const uint8_t* vt_lds = kt_lds + T::kKTile;
 
-    const bool act0 = (wq_first < N) && !(CAUSAL && k0 > wq_first + 31);
-    const bool act1 = (wq_first + 32 < N) && !(CAUSAL && k0 > wq_first + 63);
-    if (act0 || act1) {
-      f32x16_t s0[2], s1[2];
-      u32x4_t pf0[2][2], pf1[2][2];
-      const bool mask0 = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > wq_first);
-      const bool mask1 = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > wq_first + 32);
-      // half 0's softmax can run while half 1's scores are on the matrix cores
-      if (act0) scores(kt_lds, 0, s0);
-      if (act1) scores(kt_lds, 1, s1);
-      if (act0) softmax_half(s0, 0, k0, mask0, pf0);
-      if (act1) softmax_half(s1, 1, k0, mask1, pf1);
-      // O^T += V^T P^T; each V operand is read once and used by both halves
+    bool act[BLOCKS], msk[BLOCKS];
+    bool any_act = false;
+#pragma unroll
+    for (int hf = 0; hf < BLOCKS; ++hf) {
+      const int first = wq_first + 32 * hf;
+      act[hf] = (first < N) && !(CAUSAL && k0 > first + 31);
+      msk[hf] = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > first);
+      any_act |= act[hf];
+    }
+    if (any_act) {
+      f32x16_t sacc[BLOCKS][2];
+      u32x4_t pf[BLOCKS][2][2];
+      // block 0's softmax can run while block 1's scores are on the matrix cores
+#pragma unroll
+      for (int hf = 0; hf < BLOCKS; ++hf)
+        if (act[hf]) scores(kt_lds, hf, sacc[hf]);
+#pragma unroll
+      for (int hf = 0; hf < BLOCKS; ++hf)
+        if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], pf[hf]);
+      // O^T += V^T P^T; each V operand is read once and used by every block
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb)
 #pragma unroll
@@ -313,8 +322,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const u32x4_t a = v_operand(vt_lds, cb, kb, t);
-            if (act0) oacc[0][cb] = mfma_32x32x16_bf16(a, pf0[kb][t], oacc[0][cb]);
-            if (act1) oacc[1][cb] = mfma_32x32x16_bf16(a, pf1[kb][t], oacc[1][cb]);
+#pragma unroll
+            for (int hf = 0; hf < BLOCKS; ++hf)
+              if (act[hf]) oacc[hf][cb] = mfma_32x32x16_bf16(a, pf[hf][kb][t], oacc[hf][cb]);
           }
     }
 
@@ -326,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < BLOCKS; ++hf) {
     const float lt = pair_sum(l[hf]);
     if (qi[hf] < N) {
       const float inv = 1.f / lt;
@@ -347,16 +357,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   }
 }
 
+// Workgroup shape: waves per workgroup and 32-row blocks per wave.
+#ifndef FATTN_FWD_WAVES
+#define FATTN_FWD_WAVES 8
+#endif
+#ifndef FATTN_FWD_BLOCKS
+#define FATTN_FWD_BLOCKS 1
+#endif
+constexpr int kWaves = FATTN_FWD_WAVES;
+constexpr int kBlocks = FATTN_FWD_BLOCKS;
+
 template <int D, bool CAUSAL>
 hipError_t launch_one(const FwdArgs& a) {
+  constexpr int kBM = kWaves * 32 * kBlocks;
   const int n_qblocks = (a.N + kBM - 1) / kBM;
   const long long items = (long long)n_qblocks * a.B * a.H;
   // c > 0 lets masked scores (-inf) give exp2(-inf) = 0 directly; for scale 0
   // a c of 1e-30 changes no weight (|s| c stays far below fp32 resolution).
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg_q = a.scale < 0.f ? 1 : 0;
-  return launch_kernel(fwd_bf16_kernel<D, CAUSAL>, dim3((unsigned)items), dim3(kThreads), 0,
-                       a.stream, static_cast<const uint16_t*>(a.q),
+  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, kWaves, kBlocks>, dim3((unsigned)items),
+                       dim3(64 * kWaves), 0, a.stream, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                        static_cast<uint16_t*>(a.o), a.lse, a.B, a.H, a.Hkv, a.N, c, neg_q,
                        n_qblocks);
