@@ -18,19 +18,18 @@
 //     accumulators (AGPRs) and m, l in registers.  With R = 32 two waves share
 //     each SIMD, so one wave's softmax and LDS waits overlap the other's
 //     matrix-core work;
-//   * 64-key tiles of K and V are copied global -> LDS by the buffer unit
-//     (buffer_load_dwordx4 ... lds, 16 bytes per lane, no VGPR staging);
-//     rows past N read as zero.  Tiles are double-buffered with one barrier
-//     per tile; the copy of tile j+2 is in flight while tile j+1 waits;
-//   * LDS rows are padded (K by 16 bytes, V by 32) so that the K reads
-//     (ds_read_b128, 16 consecutive rows) and the V transpose reads
-//     (ds_read_b64_tr_b16, 8 rows x 64 bytes) avoid bank conflicts while every
-//     read address stays one base register plus an immediate; the copy points
-//     pad slots past the end of the buffer;
+//   * 64-key tiles of K are copied global -> LDS by the buffer unit
+//     (buffer_load_dwordx4 ... lds, 16 bytes per lane, no VGPR staging) into
+//     rows padded by 16 bytes (the copy points pad slots past the end of the
+//     buffer); V tiles are loaded into registers one tile ahead and stored
+//     transposed.  Rows past N read as zero.  Tiles are double-buffered with
+//     one barrier per tile;
 //   * the scores are computed transposed, S^T = K Q^T, so each lane owns one
 //     query row and the score accumulator becomes the P^T operand of
-//     O^T += V^T P^T without leaving registers.  V^T operands come straight
-//     from row-major V through the transpose read;
+//     O^T += V^T P^T without leaving registers.  Every K and V^T operand is a
+//     single conflict-free ds_read_b128 at a base register plus an immediate
+//     (a transpose read would need two instructions per operand, and LDS
+//     instruction issue, not bytes, is what bounds this loop);
 //   * the running reference is raised lazily (see softmax_block), so the
 //     common path has no cross-lane reduction and never touches O;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA; the
@@ -53,20 +52,20 @@ template <int D>
 struct Tile {
   static constexpr int kRowBytes = 2 * D;                // one bf16 row in global memory
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  // LDS rows are padded by one 16-byte slot (K) or two (V): K rows then start
-  // 4 banks apart (16 consecutive rows read with ds_read_b128 hit distinct
-  // banks), V rows 8 banks apart (the 8-row transpose reads pair up evenly).
+  // K rows in LDS are padded by one 16-byte slot, so 16 consecutive rows read
+  // with ds_read_b128 start 4 banks apart and never collide.  V is stored
+  // transposed (d-major, one row per column of V, keys permuted to match the
+  // score layout) with rows of 64 keys padded by 16 bytes (36 banks apart).
   static constexpr int kKSlots = kChunks + 1;            // 16-byte slots per K row in LDS
-  static constexpr int kVSlots = kChunks + 2;            // ... per V row
   static constexpr int kKStride = 16 * kKSlots;          // bytes
-  static constexpr int kVStride = 16 * kVSlots;
+  static constexpr int kVtStride = 2 * kBN + 16;         // bytes per V^T row
   static constexpr int kKTile = kBN * kKStride;
-  static constexpr int kVTile = kBN * kVStride;
+  static constexpr int kVTile = D * kVtStride;
   static constexpr int kKCopies = kBN * kKSlots / 64;    // wave-wide copy instructions per K tile
-  static constexpr int kVCopies = kBN * kVSlots / 64;
+  static constexpr int kVBlocks = (kBN / 4) * (D / 8);   // 4-key x 8-column V blocks per tile
   static constexpr int kKSteps = D / 16;                 // contraction steps of S^T over d
   static constexpr int kDBlocks = D / 32;                // 32-row blocks of O^T
-  static_assert((kBN * kKSlots) % 64 == 0 && (kBN * kVSlots) % 64 == 0, "whole copy instructions");
+  static_assert((kBN * kKSlots) % 64 == 0, "whole copy instructions");
 };
 
 template <int D, bool CAUSAL, int WAVES, int BLOCKS>
@@ -139,9 +138,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const int chunk = slot - row * slots_per_row;
     return chunk < T::kChunks ? row * T::kRowBytes + 16 * chunk : -1;
   };
-  auto issue_tile = [&](int k0, int buf) {
+  auto issue_k_tile = [&](int k0, int buf) {
     uint8_t* kdst = smem + buf * kStage;
-    uint8_t* vdst = kdst + T::kKTile;
     const int base = k0 * T::kRowBytes;
 #pragma unroll
     for (int j0 = 0; j0 < T::kKCopies; j0 += WAVES) {
@@ -151,17 +149,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
         buffer_load_lds16(k_rsrc, kdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
       }
     }
+  };
+  // V goes through registers so it can be stored transposed: thread = (4-key
+  // group, 8-column chunk), key group fastest, so the 8-byte transposed stores
+  // of one wave cover whole V^T rows without bank conflicts.
+  const int v_kg4 = tid & 15;
+  const int v_dc = tid >> 4;
+  const bool v_loader = tid < T::kVBlocks;
+  u32x4_t vreg[4];
+  auto load_v_tile = [&](int k0) {
+    if (v_loader) {
 #pragma unroll
-    for (int j0 = 0; j0 < T::kVCopies; j0 += WAVES) {
-      const int j = j0 + wave;
-      if (j < T::kVCopies) {
-        const int off = copy_offset(64 * j + lane, T::kVSlots);
-        buffer_load_lds16(v_rsrc, vdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[r] = buffer_load_b128(v_rsrc, (k0 + 4 * v_kg4 + r) * T::kRowBytes + 16 * v_dc);
     }
   };
-  // copy instructions of one tile issued by this wave
-  const int my_copies = (T::kKCopies - wave + WAVES - 1) / WAVES + (T::kVCopies - wave + WAVES - 1) / WAVES;
+  auto store_v_tile = [&](int buf) {
+    if (v_loader) {
+      uint16_t* vt = reinterpret_cast<uint16_t*>(smem + buf * kStage + T::kKTile);
+      store_block_transposed(vt, T::kVtStride / 2, 8 * v_dc, 4 * v_kg4, vreg);
+    }
+  };
+  // copy instructions of one K tile issued by this wave
+  const int my_copies = (T::kKCopies - wave + WAVES - 1) / WAVES;
 
   // ---- running state (log2 units), per 32-row block -------------------------
   float m2[BLOCKS], l[BLOCKS];   // l: this lane's keys only; lane pairs are summed at the end
@@ -268,25 +278,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     l[hf] += psum;
   };
 
-  // V^T operand (32 d x 16 keys) for d-block cb, key block kb, step t:
-  // two transpose reads of 4 keys each (keys 16t + 4*grp + 0..3 and +8).
-  const int tr_base = (4 * grp + ((lane & 15) >> 2)) * T::kVStride +
-                      2 * (4 * (lane & 3) + 16 * ((lane >> 4) & 1));
+  // V^T operand (32 d x 16 keys) for d-block cb, key block kb, step t: one
+  // 16-byte read of the transposed tile (keys 16t + 8*grp + 0..7 in the
+  // permuted order that matches registers 8t..8t+7 of the score accumulator).
+  const int vt_base = col * T::kVtStride + 16 * grp;
   auto v_operand = [&](const uint8_t* vt_lds, int cb, int kb, int t) {
-    const uint8_t* p = vt_lds + tr_base + (32 * kb + 16 * t) * T::kVStride + 64 * cb;
-    const u32x2_t lo = ds_read_tr16_b64(p);
-    const u32x2_t hi = ds_read_tr16_b64(p + 8 * T::kVStride);
-    return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    return *reinterpret_cast<const u32x4_t*>(vt_lds + vt_base + 32 * cb * T::kVtStride +
+                                             2 * (32 * kb + 16 * t));
   };
 
   // ---- main loop: one barrier per tile, LDS double-buffered ----------------
-  issue_tile(0, 0);
-  if (n_kt > 1) {
-    issue_tile(kBN, 1);
-    wait_vmem_leq(my_copies);   // tile 0's copies (issued first) have landed
-  } else {
-    wait_vmem_all();
-  }
+  load_v_tile(0);
+  issue_k_tile(0, 0);
+  wait_vmem_all();
+  store_v_tile(0);
+  if (n_kt > 1) issue_k_tile(kBN, 1);
   __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -294,6 +300,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const int k0 = kt * kBN;
     const uint8_t* kt_lds = smem + buf * kStage;
     const uint8_t* vt_lds = kt_lds + T::kKTile;
+    if (kt + 1 < n_kt) load_v_tile(k0 + kBN);   // lands during this tile's compute
 
     bool act[BLOCKS], msk[BLOCKS];
     bool any_act = false;
@@ -328,10 +335,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
           }
     }
 
-    // tile kt+1 must have landed and every wave must be done with buffer `buf`
+    // tile kt+1 (K copy, V registers) must have landed; V^T goes into the
+    // other buffer, which nobody has read since the previous barrier; then every
+    // wave must be done with buffer `buf` before its K is overwritten
     wait_vmem_all();
+    if (kt + 1 < n_kt) store_v_tile(buf ^ 1);
     __syncthreads();
-    if (kt + 2 < n_kt) issue_tile(k0 + 2 * kBN, buf);
+    if (kt + 2 < n_kt) issue_k_tile(k0 + 2 * kBN, buf);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
