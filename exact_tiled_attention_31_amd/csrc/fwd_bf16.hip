@@ -68,6 +68,21 @@ struct Tile {
   static_assert((kBN * kKSlots) % 64 == 0, "whole copy instructions");
 };
 
+// Ask the scheduler to keep LDS operand reads kLead matrix-core steps ahead of
+// their use in a region of n (read, MFMA) pairs: with two waves per SIMD the
+// LDS latency is otherwise exposed on almost every step.
+template <int n, int kLead = 4>
+__device__ __forceinline__ void interleave_reads_and_mfma() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kLead, 0);
+#pragma unroll
+  for (int i = 0; i < n - kLead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, kLead, 0);
+}
+
 template <int D, bool CAUSAL, int WAVES, int BLOCKS>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -197,6 +212,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
         sacc[kb] = mfma_32x32x16_bf16(a, qf[hf][s], sacc[kb]);
       }
     }
+    interleave_reads_and_mfma<2 * T::kKSteps>();
   };
 
   // softmax of one block's 32 x 64 score tile -> bf16 P^T operands; updates l.
@@ -321,18 +337,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
 #pragma unroll
       for (int hf = 0; hf < BLOCKS; ++hf)
         if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], pf[hf]);
-      // O^T += V^T P^T; each V operand is read once and used by every block
+      // O^T += V^T P^T; each V operand is read once and used by every block.
+      // The d-block loop is innermost so consecutive matrix-core operations
+      // accumulate into different registers (no back-to-back dependency).
 #pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
+          for (int cb = 0; cb < T::kDBlocks; ++cb) {
             const u32x4_t a = v_operand(vt_lds, cb, kb, t);
 #pragma unroll
             for (int hf = 0; hf < BLOCKS; ++hf)
               if (act[hf]) oacc[hf][cb] = mfma_32x32x16_bf16(a, pf[hf][kb][t], oacc[hf][cb]);
           }
+      if (BLOCKS == 1) interleave_reads_and_mfma<4 * T::kDBlocks>();
     }
 
     // tile kt+1 (K copy, V registers) must have landed; V^T goes into the
