@@ -86,6 +86,40 @@ def cpu_baseline(inp, w, heads: int):
                       f"BLAS threads {blas_threads}"}
 
 
+def backward_timing(fa, W, torch, np, dev, warmup, steps):
+    """Informational: fa_bwd on the backward workload (B=2 H=16 N=4096 d=128
+    causal), timed with HIP events on the launch stream.  The rate counts the
+    algorithmic work of the gradient, 2.5x the causal-adjusted forward flops
+    (five N x N x d contractions instead of two)."""
+    w5 = W.C5
+    inp = W.gen_inputs(w5)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (to_dev(getattr(inp, n + "_bits")) for n in ("q", "k", "v", "do"))
+    stream = torch.cuda.current_stream(dev)
+    o, lse = fa.fa_fwd(q, k, v, causal=True, scale=w5.scale, stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(16, fa.fa_bwd_workspace_bytes(w5.B, w5.H, w5.Hkv, w5.N, w5.d)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=w5.scale, stream=stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=w5.scale, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    flops = 2.5 * w5.causal_adjusted_flops()
+    return {"workload": "backward B=2 H=16 Hkv=16 N=4096 d=128 bf16 causal (seed 5)",
+            "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "flop_convention": "2.5 * 4*B*H*N^2*d/2", "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +128,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the informational backward timing (B=2 H=16 N=4096 d=128 causal)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -176,6 +212,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
     }
+    if not args.no_backward:
+        out["backward"] = backward_timing(fa, W, torch, np, dev, args.warmup, max(5, args.steps // 5))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads)
     print(json.dumps(out), flush=True)
