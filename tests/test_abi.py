@@ -80,6 +80,10 @@ def test_forward_validation(f32):
         assert fwd(lib, f32=f32, **kw) == INV, kw
     for d in (32, 96, 256):
         assert fwd(lib, f32=f32, d=d) == UNS, d
+    if not f32:
+        # one head's bf16 K/V slab (N*d*2 bytes) must stay below 2^31
+        for n, d in ((1 << 23, 128), (1 << 24, 64)):
+            assert fwd(lib, H=1, Hkv=1, N=n, d=d) == INV, (n, d)
     # empty problems are a no-op and may pass NULL pointers
     for kw in ({"B": 0}, {"N": 0}):
         assert fwd(lib, f32=f32, q=None, k=None, v=None, o=None, lse=None, **kw) == fa.FA_OK
