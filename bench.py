@@ -7,8 +7,9 @@ heads, N=8192, d=128, bf16 storage, causal, scale 1/sqrt(128); Q, K, V iid
 N(0,1) from seed 3 with 1% of key rows per kv head scaled x8.  Inputs are
 generated on the host, copied to HBM once, and are resident before timing.
 
-A step is one fa_fwd call over the whole batch.  W untimed warm-up steps,
-then K steps bracketed by device synchronisation on both sides.  Prints one
+A step is one fa_fwd call over the whole batch.  W untimed warm-up steps
+(about 0.1 s of work by default, enough for the clock to settle), then K
+steps bracketed by device synchronisation on both sides.  Prints one
 JSON line:
   value     causal-adjusted TFLOP/s = 4*B*H*N^2*d/2 / (wall time per step)
   roofline  the forward kernel against the dense bf16 matrix-core peak; its
@@ -123,8 +124,10 @@ def backward_timing(fa, W, torch, np, dev, warmup, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the GPU needs a few hundred ms of load to "
+                         "reach its sustained clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")

@@ -44,9 +44,12 @@ namespace {
 constexpr int kBN = 64;   // keys per tile
 constexpr float kNegInf = -__builtin_inff();
 // How far (log2 units) a row max may exceed the running reference before the
-// accumulator is rebased: terms up to 2^24 keep every fp32 sum far from
-// overflow for any realistic |V| and N.
-constexpr float kSlack = 24.f;
+// accumulator is rebased.  Terms stay below 2^48, so sums over N <= 2^31 keys
+// of p * v remain finite in fp32 for any |v| < 2^48; on inputs with rare,
+// much larger keys (1% of rows x8) a rebase after the first tile is then
+// almost never needed.
+constexpr float kSlack = 48.f;
+constexpr float kSlackSum = 281474976710656.f;   // 2^kSlack
 
 template <int D>
 struct Tile {
@@ -94,8 +97,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   // [buffer][K tile | V tile]
   constexpr int kStage = T::kKTile + T::kVTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
-  // per-wave scratch for the rare rebase of the output accumulator
-  __shared__ __attribute__((aligned(16))) float rescale_scratch[WAVES * 64 * 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,13 +217,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   };
 
   // softmax of one block's 32 x 64 score tile -> bf16 P^T operands; updates l.
-  // The running reference m (log2 units) is raised lazily: exp2(s*c - m) may
-  // exceed 1 by up to 2^kSlack before m is moved, so the accumulator is
-  // rebased only when some row's max outgrows m by more than kSlack.  O and l
-  // always share m, so the result is the same; fp32 holds the larger terms.
-  // c > 0 always (the host clamps it), so masked scores of -inf give
-  // exp2(-inf) = 0 without a select.
-  auto softmax_block = [&](f32x16_t (&sacc)[2], int hf, int k0, bool need_mask,
+  // The running reference m (log2 units) is set to the row max on the first
+  // tile (key tile 0, which holds key 0, visible to every row) and afterwards
+  // raised only when needed: exp2(s*c - m) may exceed 1, and the tile is
+  // accepted as long as this lane's terms sum to at most 2^kSlack (so no term
+  // is larger).  Otherwise the reference is raised to the row max, l and O are
+  // rebased by exp2(m_old - m_new) and the tile's terms are recomputed.  O and
+  // l always share m, so the result is the same; fp32 holds the larger terms.
+  // l sums the fp32 weights (the saved LSE must not carry the bf16 rounding
+  // of the weights that multiply V).  c > 0 always (the host clamps it), so
+  // masked scores of -inf give exp2(-inf) = 0 without a select.
+  auto softmax_block = [&](f32x16_t (&sacc)[2], int hf, int k0, bool need_mask, bool first,
                            u32x4_t (&pf)[2][2]) {
     if (need_mask) {
       asm volatile("" ::: "memory");   // a real branch: unmasked tiles pay nothing
@@ -236,60 +241,41 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
         }
       }
     }
-    float smax = kNegInf;
+    auto row_max = [&]() {
+      float smax = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
-    if (__builtin_expect(__any(smax * c > m2[hf] + kSlack), 0)) {
-      // raise the reference to the row max and rebase what is held
+        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
+      return pair_max(smax) * c;
+    };
+    if (first) m2[hf] = row_max();
+    auto weights = [&]() {
+      const float m = m2[hf];
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(fmaf(sacc[kb][r], c, -m));
+          if (r & 1) sb += p[r]; else sa += p[r];
+        }
+        pf[kb][0] = pack_bf16x8(&p[0]);
+        pf[kb][1] = pack_bf16x8(&p[8]);
+      }
+      return sa + sb;
+    };
+    float psum = weights();
+    if (__builtin_expect(__any(psum > kSlackSum), 0)) {
       asm volatile("" ::: "memory");
-      const float m_new = fmaxf(m2[hf], pair_max(smax) * c);
-      // 0 while nothing was seen; 1 for a row that is still entirely masked
-      const float corr = (m_new == kNegInf) ? 1.f : fast_exp2(m2[hf] - m_new);
+      const float m_new = fmaxf(m2[hf], row_max());
+      const float corr = fast_exp2(m2[hf] - m_new);
       l[hf] *= corr;
-      // The accumulator lives in AGPRs, which the VALU cannot read; it goes
-      // through LDS (which moves AGPR data directly) to be scaled, so that no
-      // VALU use of it exists and it never has to be held in VGPRs.
-      volatile f32x4_t* scr =
-          reinterpret_cast<volatile f32x4_t*>(rescale_scratch) + wave * 64 * 4 + lane;
 #pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4_t x = {oacc[hf][cb][4 * q4], oacc[hf][cb][4 * q4 + 1], oacc[hf][cb][4 * q4 + 2],
-                       oacc[hf][cb][4 * q4 + 3]};
-          scr[64 * q4] = x;
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          f32x4_t x = scr[64 * q4];
-          x *= corr;
-          scr[64 * q4] = x;
-        }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t x = scr[64 * q4];
-          oacc[hf][cb][4 * q4] = x[0];
-          oacc[hf][cb][4 * q4 + 1] = x[1];
-          oacc[hf][cb][4 * q4 + 2] = x[2];
-          oacc[hf][cb][4 * q4 + 3] = x[3];
-        }
-      }
+      for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] *= corr;
       m2[hf] = m_new;
-    }
-    const float m_use = (m2[hf] == kNegInf) ? 0.f : m2[hf];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(sacc[kb][r], c, -m_use));
-        psum += p[r];
-      }
-      pf[kb][0] = pack_bf16x8(&p[0]);
-      pf[kb][1] = pack_bf16x8(&p[8]);
+      psum = weights();
     }
     l[hf] += psum;
   };
@@ -336,7 +322,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
         if (act[hf]) scores(kt_lds, hf, sacc[hf]);
 #pragma unroll
       for (int hf = 0; hf < BLOCKS; ++hf)
-        if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], pf[hf]);
+        if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], kt == 0, pf[hf]);
       // O^T += V^T P^T; each V operand is read once and used by every block.
       // The d-block loop is innermost so consecutive matrix-core operations
       // accumulate into different registers (no back-to-back dependency).
