@@ -8,7 +8,7 @@ keys after the query to minus infinity; "How FlashAttention Uses Tiling",
 softmax equation):
 
     s_ij   = scale * sum_c q[b,h,i,c] * k[b,g,j,c]         g = h // (H / Hkv)
-    valid  = (not causal) or j <= i
+    valid  = ((not causal) or j <= i) and (window is None or i - j < window)
     m_i    = max over valid j of s_ij
     l_i    = sum over valid j of exp(s_ij - m_i)
     O_i    = sum over valid j of exp(s_ij - m_i) * v[b,g,j,:] / l_i
@@ -21,6 +21,11 @@ Readings where the pages are silent (stated once here, listed in the design doc):
   * The scale multiplies Q K^T before the max is taken.
   * A row with no visible key (impossible for square causal or non-causal
     attention with N >= 1) is defined as O = 0, LSE = -inf.
+
+The local (sliding-window) variant is the approximation the same page sets
+against exact attention in section 5: query i sees only the keys
+i - window + 1 .. i (window >= 1; causal is implied).  With window >= N it is
+causal attention; with window = 1 every row returns its own value row.
 
 The backward is the calculus of the same definition (the pages say only that
 it recomputes the probabilities from Q, K, V and the saved statistics,
@@ -63,14 +68,26 @@ def _check(q, k, v):
     return B, H, Hkv, N, d
 
 
+def _check_window(causal: bool, window):
+    if window is None:
+        return
+    if not causal:
+        raise ValueError("a window implies causal attention")
+    if int(window) < 1:
+        raise ValueError("window must be >= 1")
+
+
 def _scores(qb: np.ndarray, kk: np.ndarray, rows: np.ndarray, causal: bool,
-            scale: float) -> np.ndarray:
+            scale: float, window=None, k0: int = 0) -> np.ndarray:
     """scale * q_rows . k^T with invisible pairs set to -inf.
-    ``rows`` holds the absolute query index of each row of ``qb``."""
+    ``rows`` holds the absolute query index of each row of ``qb``; ``kk``
+    holds keys k0, k0 + 1, ... ."""
     s = scale * (qb @ kk.T)
+    cols = k0 + np.arange(kk.shape[0])
     if causal:
-        cols = np.arange(kk.shape[0])
         s[cols[None, :] > rows[:, None]] = -np.inf
+    if window is not None:
+        s[cols[None, :] <= rows[:, None] - window] = -np.inf
     return s
 
 
@@ -84,12 +101,14 @@ def _normalise(s: np.ndarray):
     return m, e, l, dead
 
 
-def attention_fwd(q, k, v, causal: bool, scale: float, row_block: int = 1024):
-    """O [B,H,N,d] and LSE [B,H,N] of the definition, float64."""
+def attention_fwd(q, k, v, causal: bool, scale: float, row_block: int = 1024, window=None):
+    """O [B,H,N,d] and LSE [B,H,N] of the definition, float64 (``window``
+    selects the local variant)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, Hkv, N, d = _check(q, k, v)
+    _check_window(causal, window)
     O = np.zeros((B, H, N, d), dtype=np.float64)
     LSE = np.full((B, H, N), -np.inf, dtype=np.float64)
     for b in range(B):
@@ -98,11 +117,13 @@ def attention_fwd(q, k, v, causal: bool, scale: float, row_block: int = 1024):
             for r0 in range(0, N, row_block):
                 r1 = min(N, r0 + row_block)
                 kmax = r1 if causal else N   # later keys are invisible to every row
+                kmin = 0 if window is None else max(0, r0 - window + 1)   # and older ones
                 rows = np.arange(r0, r1)
-                s = _scores(q[b, h, r0:r1], k[b, g, :kmax], rows, causal, scale)
+                s = _scores(q[b, h, r0:r1], k[b, g, kmin:kmax], rows, causal, scale, window,
+                            kmin)
                 m, e, l, dead = _normalise(s)
                 with np.errstate(divide="ignore", invalid="ignore"):
-                    o = (e @ v[b, g, :kmax]) / l[:, None]
+                    o = (e @ v[b, g, kmin:kmax]) / l[:, None]
                     lse = m + np.log(l)
                 o[dead] = 0.0
                 lse[dead] = -np.inf
@@ -111,7 +132,7 @@ def attention_fwd(q, k, v, causal: bool, scale: float, row_block: int = 1024):
     return O, LSE
 
 
-def attention_rows(q, k, v, causal: bool, scale: float, rows):
+def attention_rows(q, k, v, causal: bool, scale: float, rows, window=None):
     """O and LSE for selected (b, h, i) query rows only (for full-size checks).
 
     ``rows`` is an int array [n, 3] of (b, h, i).  Returns O [n, d], LSE [n].
@@ -121,16 +142,18 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows):
     k = np.asarray(k)
     v = np.asarray(v)
     B, H, Hkv, N, d = _check(q, k, v)
+    _check_window(causal, window)
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     O = np.zeros((rows.shape[0], d), dtype=np.float64)
     LSE = np.full(rows.shape[0], -np.inf, dtype=np.float64)
     for n, (b, h, i) in enumerate(rows):
         g = kv_head_of(int(h), H, Hkv)
         kmax = int(i) + 1 if causal else N
-        kk = k[b, g, :kmax].astype(np.float64)
-        vv = v[b, g, :kmax].astype(np.float64)
+        kmin = 0 if window is None else max(0, int(i) - window + 1)
+        kk = k[b, g, kmin:kmax].astype(np.float64)
+        vv = v[b, g, kmin:kmax].astype(np.float64)
         qi = q[b, h, i].astype(np.float64)[None, :]
-        s = _scores(qi, kk, np.array([i]), causal, scale)
+        s = _scores(qi, kk, np.array([i]), causal, scale, window, kmin)
         m, e, l, dead = _normalise(s)
         if dead[0]:
             continue
