@@ -121,6 +121,30 @@ def backward_timing(fa, W, torch, np, dev, warmup, steps):
             "flop_convention": "2.5 * 4*B*H*N^2*d/2", "steps": steps}
 
 
+def local_timing(fa, w, torch, q, k, v, stream, window, warmup, steps):
+    """Informational: fa_fwd_local (window 256, the pages' example width) on
+    the headline inputs, timed with HIP events on the launch stream.  The rate
+    counts 4*d flops per visible (query, key) pair: sum_i min(i+1, window)
+    pairs per head."""
+    n = w.N
+    pairs = window * (window + 1) // 2 + (n - window) * window if n > window else n * (n + 1) // 2
+    flops = 4.0 * w.d * w.B * w.H * pairs
+    for _ in range(warmup):
+        fa.fa_fwd_local(q, k, v, window, scale=w.scale, stream=stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        fa.fa_fwd_local(q, k, v, window, scale=w.scale, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    return {"workload": f"local causal forward, window {window}, same inputs as the headline",
+            "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "flop_convention": "4*d*B*H*sum_i min(i+1, window)", "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +155,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")
+    ap.add_argument("--no-local", action="store_true",
+                    help="skip the informational sliding-window timing (window 256)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the informational backward timing (B=2 H=16 N=4096 d=128 causal)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -215,6 +241,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
     }
+    if not args.no_local:
+        out["local"] = local_timing(fa, w, torch, q, k, v, stream, 256, args.warmup, args.steps)
     if not args.no_backward:
         out["backward"] = backward_timing(fa, W, torch, np, dev, args.warmup, max(5, args.steps // 5))
     if not args.no_cpu_baseline:

@@ -8,6 +8,7 @@ an exception is raised.
 Names mirror the C ABI in ``include/fattn.h``:
     fa_fwd(q, k, v, ...)        bf16 forward  -> (o, lse)
     fa_fwd_f32(q, k, v, ...)    fp32 forward  -> (o, lse)
+    fa_fwd_local(q, k, v, window, ...)  bf16 sliding-window causal forward -> (o, lse)
     fa_bwd(q, k, v, o, lse, dO, ...)  bf16 backward -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     fa_status_string(status)
@@ -33,6 +34,7 @@ _F = ctypes.c_float
 PROTOTYPES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_local": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -117,7 +119,9 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _fwd(cname, dtype, q, k, v, o, lse, causal, scale, stream):
+def _fwd(cname, dtype, q, k, v, o, lse, mode: int, scale, stream):
+    """Shared marshalling; ``mode`` is the call's int argument after d (causal
+    flag or window)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, dtype)
@@ -131,7 +135,7 @@ def _fwd(cname, dtype, q, k, v, o, lse, causal, scale, stream):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = getattr(lib(), cname)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               B, H, Hkv, N, d, int(bool(causal)), float(scale),
+                               B, H, Hkv, N, d, int(mode), float(scale),
                                _stream_of(q, stream))
     if st != FA_OK:
         raise FattnError(st, cname)
@@ -143,13 +147,21 @@ def fa_fwd(q, k, v, o=None, lse=None, causal: bool = False, scale: float | None 
     """bf16 forward.  q [B,H,N,d], k, v [B,Hkv,N,d] (torch.bfloat16, contiguous,
     on the GPU).  Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N]); o and lse are
     allocated when not given.  scale defaults to 1/sqrt(d)."""
-    return _fwd("fa_fwd", _torch().bfloat16, q, k, v, o, lse, causal, scale, stream)
+    return _fwd("fa_fwd", _torch().bfloat16, q, k, v, o, lse, int(bool(causal)), scale, stream)
+
+
+def fa_fwd_local(q, k, v, window: int, o=None, lse=None, scale: float | None = None,
+                 stream=None):
+    """bf16 local (sliding-window) causal forward: query i sees keys
+    i - window + 1 .. i.  Same tensors and defaults as fa_fwd."""
+    return _fwd("fa_fwd_local", _torch().bfloat16, q, k, v, o, lse, int(window), scale, stream)
 
 
 def fa_fwd_f32(q, k, v, o=None, lse=None, causal: bool = False, scale: float | None = None,
                stream=None):
     """fp32 forward (same contract as fa_fwd with torch.float32 tensors)."""
-    return _fwd("fa_fwd_f32", _torch().float32, q, k, v, o, lse, causal, scale, stream)
+    return _fwd("fa_fwd_f32", _torch().float32, q, k, v, o, lse, int(bool(causal)), scale,
+                stream)
 
 
 def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
@@ -187,6 +199,6 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
     return dq, dk, dv
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
            "FattnError", "lib", "LIB_PATH", "PROTOTYPES",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]

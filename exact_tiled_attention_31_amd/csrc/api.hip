@@ -78,6 +78,17 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   return status_of(launch_fwd_bf16(a));
 }
 
+extern "C" int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Hkv, int N, int d, int window, float scale,
+                            hipStream_t stream) {
+  bool empty = false;
+  int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, 2, &empty);
+  if (st != FA_OK || empty) return st;
+  if (window < 1) return FA_ERR_INVALID_ARG;
+  FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, true, scale, stream, window};
+  return status_of(launch_fwd_bf16(a));
+}
+
 extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int H, int Hkv, int N, int d, int causal, float scale,
                           hipStream_t stream) {

@@ -86,11 +86,14 @@ __device__ __forceinline__ void interleave_reads_and_mfma() {
   __builtin_amdgcn_sched_group_barrier(kMfma, kLead, 0);
 }
 
-template <int D, bool CAUSAL, int WAVES, int BLOCKS>
+// LOCAL (which implies CAUSAL): query i sees keys i - window + 1 .. i only;
+// key tiles older than every row of the workgroup are never loaded.
+template <int D, bool CAUSAL, bool LOCAL, int WAVES, int BLOCKS>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks) {
+    int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks, int window) {
+  static_assert(CAUSAL || !LOCAL, "local attention is causal");
   using T = Tile<D>;
   constexpr int kRowsPerWave = 32 * BLOCKS;
   constexpr int kBM = WAVES * kRowsPerWave;
@@ -144,6 +147,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   const int q_hi = min(q0 + kBM, N);
   int n_kt = (N + kBN - 1) / kBN;
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kBN + 1);
+  // first tile holding a key that the block's first query still sees
+  const int kt_begin = LOCAL ? max(0, q0 - window + 1) / kBN : 0;
 
   // ---- tile copy: wave-wide instruction j fills LDS slots 64j .. 64j+63 ------
   // (lane order).  Slot -> (row, chunk) of the padded layout; pad slots and rows
@@ -236,7 +241,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * grp + (r & 3);
-          const bool dead = (kj >= N) || (CAUSAL && kj > qi[hf]);
+          const bool dead =
+              (kj >= N) || (CAUSAL && kj > qi[hf]) || (LOCAL && qi[hf] - kj >= window);
           if (dead) sacc[kb][r] = kNegInf;
         }
       }
@@ -249,9 +255,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
       return pair_max(smax) * c;
     };
-    if (first) m2[hf] = row_max();
+    if (LOCAL) {
+      // a row's first visible key may lie in any tile: take the row max on
+      // the first tile that shows the row a key (m2 stays -inf until then)
+      if (__any(m2[hf] == kNegInf)) {
+        const float mx = row_max();
+        if (m2[hf] == kNegInf) m2[hf] = mx;
+      }
+    } else if (first) {
+      m2[hf] = row_max();
+    }
     auto weights = [&]() {
-      const float m = m2[hf];
+      // a row that has seen no key yet has only -inf scores here: reference 0
+      const float m = (LOCAL && m2[hf] == kNegInf) ? 0.f : m2[hf];
       float sa = 0.f, sb = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -270,7 +286,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     if (__builtin_expect(__any(psum > kSlackSum), 0)) {
       asm volatile("" ::: "memory");
       const float m_new = fmaxf(m2[hf], row_max());
-      const float corr = fast_exp2(m2[hf] - m_new);
+      // 1 for a row that has still seen no key (l and O are 0 there)
+      const float corr = (m_new == kNegInf) ? 1.f : fast_exp2(m2[hf] - m_new);
       l[hf] *= corr;
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] *= corr;
@@ -290,15 +307,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   };
 
   // ---- main loop: one barrier per tile, LDS double-buffered ----------------
-  load_v_tile(0);
-  issue_k_tile(0, 0);
+  load_v_tile(kt_begin * kBN);
+  issue_k_tile(kt_begin * kBN, 0);
   wait_vmem_all();
   store_v_tile(0);
-  if (n_kt > 1) issue_k_tile(kBN, 1);
+  if (kt_begin + 1 < n_kt) issue_k_tile((kt_begin + 1) * kBN, 1);
   __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt_begin; kt < n_kt; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
     const int k0 = kt * kBN;
     const uint8_t* kt_lds = smem + buf * kStage;
     const uint8_t* vt_lds = kt_lds + T::kKTile;
@@ -309,8 +326,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int hf = 0; hf < BLOCKS; ++hf) {
       const int first = wq_first + 32 * hf;
-      act[hf] = (first < N) && !(CAUSAL && k0 > first + 31);
-      msk[hf] = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > first);
+      act[hf] = (first < N) && !(CAUSAL && k0 > first + 31) &&
+                !(LOCAL && first - (k0 + kBN - 1) >= window);
+      msk[hf] = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > first) ||
+                (LOCAL && first + 31 - k0 >= window);
       any_act |= act[hf];
     }
     if (any_act) {
@@ -382,7 +401,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
 constexpr int kWaves = FATTN_FWD_WAVES;
 constexpr int kBlocks = FATTN_FWD_BLOCKS;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL>
 hipError_t launch_one(const FwdArgs& a) {
   constexpr int kBM = kWaves * 32 * kBlocks;
   const int n_qblocks = (a.N + kBM - 1) / kBM;
@@ -391,18 +410,24 @@ hipError_t launch_one(const FwdArgs& a) {
   // a c of 1e-30 changes no weight (|s| c stays far below fp32 resolution).
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg_q = a.scale < 0.f ? 1 : 0;
-  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, kWaves, kBlocks>, dim3((unsigned)items),
-                       dim3(64 * kWaves), 0, a.stream, static_cast<const uint16_t*>(a.q),
-                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                       static_cast<uint16_t*>(a.o), a.lse, a.B, a.H, a.Hkv, a.N, c, neg_q,
-                       n_qblocks);
+  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, LOCAL, kWaves, kBlocks>,
+                       dim3((unsigned)items), dim3(64 * kWaves), 0, a.stream,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                       a.B, a.H, a.Hkv, a.N, c, neg_q, n_qblocks, a.window);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_one<128, true>(a) : launch_one<128, false>(a);
-  return a.causal ? launch_one<64, true>(a) : launch_one<64, false>(a);
+  // a window covering the whole sequence is plain causal attention
+  const bool local = a.causal && a.window > 0 && a.window < a.N;
+  if (a.d == 128) {
+    if (local) return launch_one<128, true, true>(a);
+    return a.causal ? launch_one<128, true, false>(a) : launch_one<128, false, false>(a);
+  }
+  if (local) return launch_one<64, true, true>(a);
+  return a.causal ? launch_one<64, true, false>(a) : launch_one<64, false, false>(a);
 }
 
 }  // namespace fattn

@@ -20,6 +20,7 @@ struct FwdArgs {
   bool causal;
   float scale;
   hipStream_t stream;
+  int window = 0;   // > 0: local attention, query i sees keys i - window + 1 .. i
 };
 
 struct BwdArgs {

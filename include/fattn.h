@@ -75,6 +75,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            hipStream_t stream);
 
 /*
+ * Local (sliding-window) causal forward, bf16 storage: query i sees only the
+ * keys i - window + 1 .. i.  This is the approximation that "LLM Architecture
+ * Refresh [3]: Flash Attention Is Exact", section 5, contrasts with exact
+ * attention; key tiles wholly before every row's window are skipped like the
+ * future tiles of causal attention (section 7).  Same layout, precision and
+ * errors as fa_fwd, plus FA_ERR_INVALID_ARG for window < 1 (checked after the
+ * empty-problem test).  window >= N gives exactly fa_fwd with causal = 1.
+ */
+int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, int window, float scale,
+                 hipStream_t stream);
+
+/*
  * Forward, fp32 storage and fp32 arithmetic throughout (the variant for
  * single-precision inputs; same operation, layout and errors as fa_fwd).
  */

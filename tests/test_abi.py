@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"])
+        ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_bwd", "fa_bwd_workspace_bytes",
+         "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -87,6 +88,25 @@ def test_forward_validation(f32):
     # empty problems are a no-op and may pass NULL pointers
     for kw in ({"B": 0}, {"N": 0}):
         assert fwd(lib, f32=f32, q=None, k=None, v=None, o=None, lse=None, **kw) == fa.FA_OK
+
+
+def test_local_validation():
+    fa, lib = _lib()
+    INV = fa.FA_ERR_INVALID_ARG
+
+    def loc(window=16, **kw):
+        a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=4, Hkv=2, N=128, d=128,
+                 scale=0.1)
+        a.update(kw)
+        return lib.fa_fwd_local(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                a["Hkv"], a["N"], a["d"], window, a["scale"], None)
+
+    for w in (0, -1, -(1 << 30)):
+        assert loc(window=w) == INV, w
+    for kw in ({"q": None}, {"o": P[0]}, {"H": 3}, {"scale": float("nan")}):
+        assert loc(**kw) == INV, kw
+    assert loc(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert loc(N=0, window=0, q=None) == fa.FA_OK        # empty problem first
 
 
 def test_backward_validation():
