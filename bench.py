@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_31_amd", "csrc", f)
@@ -145,6 +146,39 @@ def local_timing(fa, w, torch, q, k, v, stream, window, warmup, steps):
             "flop_convention": "4*d*B*H*sum_i min(i+1, window)", "steps": steps}
 
 
+def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps):
+    """Informational: fa_fwd_fp8 on the headline draws quantized to e4m3 with
+    per-tensor scales (same shape, causal), HIP events on the launch stream;
+    rate against the dense fp8 matrix-core peak."""
+    w = W.F3
+    inp = W.gen_inputs(w)
+    q, k, v = (torch.from_numpy(getattr(inp, n + "_codes")).to(dev) for n in ("q", "k", "v"))
+    ds = inp.descale
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def call():
+        fa.fa_fwd_fp8(q, k, v, ds["q"], ds["k"], ds["v"], o=o, lse=lse, causal=True,
+                      scale=w.scale, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    tf = w.causal_adjusted_flops() / (ms * 1e-3) / 1e12
+    return {"workload": "fp8 e4m3 forward, headline shape and draws, per-tensor scales",
+            "ms": round(ms, 5), "tflops": round(tf, 2), "peak_fp8": PEAK_FP8_TFLOPS,
+            "frac": round(tf / PEAK_FP8_TFLOPS, 4), "flop_convention": "4*B*H*N^2*d/2",
+            "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +189,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the informational FP8 forward timing")
     ap.add_argument("--no-local", action="store_true",
                     help="skip the informational sliding-window timing (window 256)")
     ap.add_argument("--no-backward", action="store_true",
@@ -241,6 +277,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
     }
+    if not args.no_fp8:
+        out["fp8"] = fp8_timing(fa, W, torch, np, dev, stream, args.warmup, args.steps)
     if not args.no_local:
         out["local"] = local_timing(fa, w, torch, q, k, v, stream, 256, args.warmup, args.steps)
     if not args.no_backward:

@@ -9,6 +9,7 @@ Names mirror the C ABI in ``include/fattn.h``:
     fa_fwd(q, k, v, ...)        bf16 forward  -> (o, lse)
     fa_fwd_f32(q, k, v, ...)    fp32 forward  -> (o, lse)
     fa_fwd_local(q, k, v, window, ...)  bf16 sliding-window causal forward -> (o, lse)
+    fa_fwd_fp8(q, k, v, dq, dk, dv, ...)  FP8 (e4m3) forward -> (o bf16, lse)
     fa_bwd(q, k, v, o, lse, dO, ...)  bf16 backward -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     fa_status_string(status)
@@ -35,6 +36,7 @@ PROTOTYPES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_local": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -157,6 +159,35 @@ def fa_fwd_local(q, k, v, window: int, o=None, lse=None, scale: float | None = N
     return _fwd("fa_fwd_local", _torch().bfloat16, q, k, v, o, lse, int(window), scale, stream)
 
 
+def fa_fwd_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float, o=None, lse=None,
+               causal: bool = False, scale: float | None = None, stream=None):
+    """FP8 forward.  q [B,H,N,d], k, v [B,Hkv,N,d] hold OCP e4m3 codes
+    (torch.uint8 or torch.float8_e4m3fn, contiguous, on the GPU) whose values
+    are descale_x * e4m3(code).  Returns (o bf16 [B,H,N,d], lse fp32
+    [B,H,N]), allocated when not given.  scale defaults to 1/sqrt(d)."""
+    torch = _torch()
+    allowed = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in allowed:
+            raise TypeError(f"{name} must be torch.uint8 or torch.float8_e4m3fn codes")
+        _need(t, name, t.dtype)
+    B, H, Hkv, N, d = _dims(q, k, v)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, (B, H, N, d))
+    _need(lse, "lse", torch.float32, (B, H, N))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                          int(bool(causal)), float(scale), float(descale_q), float(descale_k),
+                          float(descale_v), _stream_of(q, stream))
+    if st != FA_OK:
+        raise FattnError(st, "fa_fwd_fp8")
+    return o, lse
+
+
 def fa_fwd_f32(q, k, v, o=None, lse=None, causal: bool = False, scale: float | None = None,
                stream=None):
     """fp32 forward (same contract as fa_fwd with torch.float32 tensors)."""
@@ -199,6 +230,6 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
     return dq, dk, dv
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
            "FattnError", "lib", "LIB_PATH", "PROTOTYPES",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]

@@ -17,7 +17,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfattn.so")
-SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "bwd_bf16.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code on purpose.

@@ -42,7 +42,9 @@ int check_sizes(int B, int H, int Hkv, int N, int d, bool* empty) {
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-              int B, int H, int Hkv, int N, int d, float scale, size_t elem, bool* empty) {
+              int B, int H, int Hkv, int N, int d, float scale, size_t elem, bool* empty,
+              size_t out_elem = 0) {
+  if (out_elem == 0) out_elem = elem;
   int st = check_sizes(B, H, Hkv, N, d, empty);
   if (st != FA_OK || *empty) return st;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
@@ -53,9 +55,10 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
     return FA_ERR_INVALID_ARG;
   const long double qbytes = (long double)B * H * N * d * elem;
   const long double kvbytes = (long double)B * Hkv * N * d * elem;
+  const long double obytes = (long double)B * H * N * d * out_elem;
   const long double lbytes = (long double)B * H * N * 4;
   const Range rq = range_of(q, qbytes), rk = range_of(k, kvbytes), rv = range_of(v, kvbytes);
-  const Range ro = range_of(o, qbytes), rl = range_of(lse, lbytes);
+  const Range ro = range_of(o, obytes), rl = range_of(lse, lbytes);
   if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv)) return FA_ERR_INVALID_ARG;
   if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv) || overlaps(rl, ro))
     return FA_ERR_INVALID_ARG;
@@ -87,6 +90,21 @@ extern "C" int fa_fwd_local(const void* q, const void* k, const void* v, void* o
   if (window < 1) return FA_ERR_INVALID_ARG;
   FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, true, scale, stream, window};
   return status_of(launch_fwd_bf16(a));
+}
+
+extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Hkv, int N, int d, int causal, float scale,
+                          float descale_q, float descale_k, float descale_v,
+                          hipStream_t stream) {
+  bool empty = false;
+  int st = check_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, 1, &empty, 2);
+  if (st != FA_OK || empty) return st;
+  for (float s : {descale_q, descale_k, descale_v})
+    if (!(isfinite(s) && s > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID_ARG;
+  Fp8FwdArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale,
+               descale_q, descale_k, descale_v, stream};
+  return status_of(launch_fwd_fp8(a));
 }
 
 extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

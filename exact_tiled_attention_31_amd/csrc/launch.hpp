@@ -40,7 +40,21 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// FP8 (OCP e4m3) forward: q, k, v hold codes whose values are descale * e4m3(code).
+struct Fp8FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;     // bf16
+  float* lse;
+  int B, H, Hkv, N, d;
+  bool causal;
+  float scale, descale_q, descale_k, descale_v;
+  hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
 

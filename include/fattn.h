@@ -88,6 +88,27 @@ int fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* ls
                  hipStream_t stream);
 
 /*
+ * FP8 forward: q, k, v hold OCP e4m3 codes (one byte per element, same
+ * [B, H, N, d] / [B, Hkv, N, d] layouts) whose values are descale_q * e4m3(q)
+ * and likewise for k and v (per-tensor scales, each finite and > 0); o is
+ * bf16 and lse fp32 as in fa_fwd, for the scores scale * q_i . k_j of those
+ * values.  Both products run on the fp8 matrix cores with fp32 accumulation;
+ * the attention weights are rounded to e4m3 before they multiply V (the
+ * low-precision variant "LLM Architecture Refresh [3]: Flash Attention Is
+ * Exact", section 8, credits to FlashAttention-3).  With e_i the largest
+ * score error of row i (the fp8 matrix cores sum each 64-term step within
+ * 2^-11 of the sum of |q_ic k_jc|), the extra error is bounded elementwise by
+ * (2^-4 + 2 e_i) (P|V|)_ic + 2^-16 sum_j |v_jc| plus the bf16 rounding of O,
+ * and that of lse by e_i (no fp8 rounding of the weights reaches lse).
+ * The 16-byte alignment rule
+ * applies to q, k, v, o; errors as fa_fwd, plus FA_ERR_INVALID_ARG for a
+ * descale that is not finite and positive.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, int causal, float scale,
+               float descale_q, float descale_k, float descale_v, hipStream_t stream);
+
+/*
  * Forward, fp32 storage and fp32 arithmetic throughout (the variant for
  * single-precision inputs; same operation, layout and errors as fa_fwd).
  */

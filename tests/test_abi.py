@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_bwd", "fa_bwd_workspace_bytes",
-         "fa_status_string"])
+        ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd",
+         "fa_bwd_workspace_bytes", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,6 +107,28 @@ def test_local_validation():
         assert loc(**kw) == INV, kw
     assert loc(d=96) == fa.FA_ERR_UNSUPPORTED
     assert loc(N=0, window=0, q=None) == fa.FA_OK        # empty problem first
+
+
+def test_fp8_validation():
+    fa, lib = _lib()
+    INV = fa.FA_ERR_INVALID_ARG
+
+    def f8(**kw):
+        a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=4, Hkv=2, N=128, d=128,
+                 causal=1, scale=0.1, dq=0.01, dk=0.02, dv=0.03)
+        a.update(kw)
+        return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                              a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dq"],
+                              a["dk"], a["dv"], None)
+
+    for kw in ({"dq": 0.0}, {"dk": -1.0}, {"dv": float("nan")}, {"dq": float("inf")},
+               {"scale": float("inf")}, {"scale": 1e30, "dq": 1e20, "dk": 1e20},
+               {"q": None}, {"lse": None}, {"H": 3},
+               {"o": ctypes.c_void_p(A + 4096)},             # bf16 o overlapping q's bytes
+               {"q": ctypes.c_void_p(A + 8)}):
+        assert f8(**kw) == INV, kw
+    assert f8(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert f8(N=0, q=None, dq=0.0) == fa.FA_OK              # empty problem first
 
 
 def test_backward_validation():

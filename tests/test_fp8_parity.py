@@ -1,0 +1,192 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8) against the float64 oracle
+evaluated on the very values the e4m3 codes and per-tensor scales represent.
+
+Tolerance (derived from the arithmetic; the pages fix none for FP8).  Two
+roundings go beyond fp32:
+  * the fp8 matrix cores sum each 64-term step of q_i . k_j with less than
+    fp32 precision; a probe on random e4m3 codes measured at most
+    2^-12.4 sum_c |q_ic k_jc|, and 2^-11 is used, so a score is off by at most
+    e_ij = 2^-11 |scale| sum_c |q_ic k_jc|, and the row's weights by a factor
+    within 1 +- 2 e_i, e_i = max over visible j of e_ij;
+  * each weight is rounded to e4m3 before it multiplies V: half an ulp is 2^-4
+    of the weight in the normal range and 2^-10 absolute below it, with the
+    weights taken relative to a reference that makes the normaliser >= 2^6;
+plus the bf16 rounding of O.  Elementwise:
+    |O - O_ref| <= (2^-4 + 2 e_i) (P|V|) + 2^-16 sum_{visible j} |v_j|
+                   + 2^-8 |O_ref| + 1e-5
+with P|V| = the oracle's attention output for |V|, and
+    |LSE - LSE_ref| <= e_i + 1e-3.
+The plain max abs error is printed beside it.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import dev_bf16_to_f64, dev_to_f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def dev_codes(inp, torch):
+    return tuple(torch.from_numpy(np.ascontiguousarray(getattr(inp, n + "_codes"))).cuda()
+                 for n in ("q", "k", "v"))
+
+
+def run_fp8(inp, fa, torch, causal=None, scale=None):
+    q, k, v = dev_codes(inp, torch)
+    ds = inp.descale
+    o, lse = fa.fa_fwd_fp8(q, k, v, ds["q"], ds["k"], ds["v"],
+                           causal=inp.w.causal if causal is None else causal,
+                           scale=inp.w.scale if scale is None else scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def visible_abs_sums(inp, causal):
+    """sum over visible keys of |v_j|, per (b, h, i, c)."""
+    w = inp.w
+    a = np.abs(inp.v)
+    s = np.cumsum(a, axis=2) if causal else np.broadcast_to(a.sum(axis=2, keepdims=True), a.shape)
+    rep = w.H // w.Hkv
+    return np.repeat(s, rep, axis=1)
+
+
+def head_score_error_bound(q, k, scale, causal):
+    """e_i = 2^-11 |scale| max over visible j of sum_c |q_ic k_jc| for one
+    head: q [N, d], k [N, d]."""
+    aq, ak = np.abs(q), np.abs(k)
+    N = q.shape[0]
+    out = np.empty(N)
+    for r0 in range(0, N, 512):
+        r1 = min(N, r0 + 512)
+        m = aq[r0:r1] @ ak.T
+        if causal:
+            m[np.arange(N)[None, :] > np.arange(r0, r1)[:, None]] = 0.0
+        out[r0:r1] = m.max(axis=1)
+    return 2.0 ** -11 * abs(scale) * out
+
+
+def score_error_bound(inp, scale, causal, rows=None):
+    """e_i per (b, h, i), or per listed (b, h, i) row."""
+    w = inp.w
+    rep = w.H // w.Hkv
+    if rows is not None:
+        out = np.empty(len(rows))
+        for n, (b, h, i) in enumerate(rows):
+            kk = np.abs(inp.k[b, h // rep, :i + 1] if causal else inp.k[b, h // rep])
+            out[n] = np.max(kk @ np.abs(inp.q[b, h, i]))
+        return 2.0 ** -11 * abs(scale) * out
+    out = np.empty((w.B, w.H, w.N))
+    for b in range(w.B):
+        for h in range(w.H):
+            out[b, h] = head_score_error_bound(inp.q[b, h], inp.k[b, h // rep], scale, causal)
+    return out
+
+
+def check_lse8(out, ref, e, what):
+    err = np.abs(out - ref)
+    bound = e + 1e-3
+    assert np.all(err <= bound), (what, float(err.max()), float((err - bound).max()))
+    return float(err.max())
+
+
+def check_fp8(out, ref, pv, vsum, what, e=0.0):
+    err = np.abs(out - ref)
+    e = np.asarray(e)[..., None] if np.ndim(e) else e
+    bound = (2.0 ** -4 + 2 * e) * pv + 2.0 ** -16 * vsum + 2.0 ** -8 * np.abs(ref) + 1e-5
+    info = dict(max_abs=float(err.max()), max_err_over_bound=float((err / bound).max()),
+                n_over_bf16_tol=int((err > 1e-2 + 2.0 ** -8 * np.abs(ref)).sum()))
+    bad = err > bound
+    if bad.any():
+        idx = np.unravel_index(np.argmax(err / bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond the fp8 bound; worst at "
+                             f"{idx}: out={out[idx]!r} ref={ref[idx]!r} bound={bound[idx]!r} {info}")
+    print(what, info, flush=True)
+    return info
+
+
+SMALL = [
+    # name, B, H, Hkv, N, d, causal, seed
+    ("fp8_d128_causal_ragged", 2, 4, 2, 300, 128, True, 301),
+    ("fp8_d128_noncausal_ragged", 1, 4, 2, 333, 128, False, 302),
+    ("fp8_d64_causal", 1, 4, 1, 520, 64, True, 303),
+    ("fp8_d64_noncausal", 1, 2, 2, 257, 64, False, 304),
+    ("fp8_N1", 1, 2, 1, 1, 128, True, 305),
+    ("fp8_N64", 1, 2, 2, 64, 128, True, 306),
+    ("fp8_N129", 1, 2, 2, 129, 128, False, 307),
+    ("fp8_gqa8_N1000", 1, 8, 1, 1000, 128, True, 308),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases(case):
+    torch, fa = require_gpu()
+    name, B, H, Hkv, N, d, causal, seed = case
+    w = W.small_case(name, "fp8", B, H, Hkv, N, d, causal, seed)
+    inp = W.gen_inputs(w)
+    o, lse = run_fp8(inp, fa, torch)
+    O, L = oracle.attention_fwd(inp.q, inp.k, inp.v, causal, w.scale)
+    PV, _ = oracle.attention_fwd(inp.q, inp.k, np.abs(inp.v), causal, w.scale)
+    e = score_error_bound(inp, w.scale, causal)
+    info = check_fp8(dev_bf16_to_f64(o), O, PV, visible_abs_sums(inp, causal), name, e)
+    print(name, "lse max abs", check_lse8(dev_to_f64(lse), L, e, name), flush=True)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.3])
+def test_scales(scale):
+    torch, fa = require_gpu()
+    w = W.small_case(f"fp8_scale{scale}", "fp8", 1, 2, 1, 200, 128, True, 309)
+    inp = W.gen_inputs(w)
+    o, lse = run_fp8(inp, fa, torch, scale=scale)
+    O, L = oracle.attention_fwd(inp.q, inp.k, inp.v, True, scale)
+    PV, _ = oracle.attention_fwd(inp.q, inp.k, np.abs(inp.v), True, scale)
+    e = score_error_bound(inp, scale, True)
+    check_fp8(dev_bf16_to_f64(o), O, PV, visible_abs_sums(inp, True), f"scale {scale}", e)
+    check_lse8(dev_to_f64(lse), L, e, f"scale {scale}")
+
+
+def test_f3_full_size():
+    # C3's draws (32 query heads on 8 kv heads, N=8192, d=128, 1% of key rows
+    # x8) as e4m3 codes: two whole heads and 1024 sampled rows over all heads.
+    torch, fa = require_gpu()
+    w = W.F3
+    inp = W.gen_inputs(w)
+    o, lse = run_fp8(inp, fa, torch)
+    vsum_all = visible_abs_sums(inp, True)
+    for h in (0, w.H - 1):
+        g = oracle.kv_head_of(h, w.H, w.Hkv)
+        sl = (slice(None), slice(h, h + 1))
+        qh, kh, vh = inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1]
+        O, L = oracle.attention_fwd(qh, kh, vh, True, w.scale)
+        PV, _ = oracle.attention_fwd(qh, kh, np.abs(vh), True, w.scale)
+        e = head_score_error_bound(inp.q[0, h], inp.k[0, g], w.scale, True).reshape(1, 1, w.N)
+        check_fp8(dev_bf16_to_f64(o[sl]), O, PV, vsum_all[sl], f"F3 head {h}", e)
+        print(f"F3 head {h} lse max abs", check_lse8(dev_to_f64(lse[sl]), L, e, f"F3 head {h}"),
+              flush=True)
+    rng = np.random.default_rng(35)
+    hi = W.sample_rows(rng, w.H, w.N, 1024)
+    rows = np.concatenate([np.zeros((len(hi), 1), np.int64), hi], axis=1)
+    Or, Lr = oracle.attention_rows(inp.q, inp.k, inp.v, True, w.scale, rows)
+    PVr, _ = oracle.attention_rows(inp.q, inp.k, np.abs(inp.v), True, w.scale, rows)
+    og = dev_bf16_to_f64(o)
+    L = dev_to_f64(lse)
+    got = np.stack([og[b, h, i] for b, h, i in rows])
+    vs = np.stack([vsum_all[b, h, i] for b, h, i in rows])
+    e = score_error_bound(inp, w.scale, True, rows)
+    check_fp8(got, Or, PVr, vs, "F3 sampled rows", e)
+    check_lse8(np.array([L[b, h, i] for b, h, i in rows]), Lr, e, "F3 sampled rows")
+
+
+def test_deterministic_and_accepts_float8_dtype():
+    torch, fa = require_gpu()
+    w = W.small_case("fp8_det", "fp8", 1, 8, 2, 1500, 128, True, 310)
+    inp = W.gen_inputs(w)
+    q, k, v = dev_codes(inp, torch)
+    ds = inp.descale
+    o1, l1 = fa.fa_fwd_fp8(q, k, v, ds["q"], ds["k"], ds["v"], causal=True, scale=w.scale)
+    if hasattr(torch, "float8_e4m3fn"):
+        q, k, v = (t.view(torch.float8_e4m3fn) for t in (q, k, v))
+    o2, l2 = fa.fa_fwd_fp8(q, k, v, ds["q"], ds["k"], ds["v"], causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -81,3 +81,63 @@ def test_c4_sampled_rows_include_fixed_rows():
 def test_workload_counts():
     assert W.C3.causal_adjusted_flops() == pytest.approx(549.755813888e9)
     assert W.C3.compulsory_bytes() == (64 + 32 + 64 + 1) * 2 ** 20
+
+
+# ---- FP8 (OCP E4M3) storage format -----------------------------------------
+
+def test_e4m3_table_matches_the_format_definition():
+    # values fixed by the OCP 8-bit floating point format, E4M3 variant
+    t = W.E4M3_VALUES
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and np.signbit(t[0x80])
+    assert t[0x01] == 2.0 ** -9            # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9        # largest subnormal
+    assert t[0x08] == 2.0 ** -6            # smallest normal
+    assert t[0x38] == 1.0
+    assert t[0x3C] == 1.5
+    assert t[0x7E] == 448.0                # largest finite
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0xFE] == -448.0 and t[0xB8] == -1.0
+    finite = t[~np.isnan(t)]
+    assert len(finite) == 254
+    pos = t[1:0x7F]
+    assert np.all(np.diff(pos) > 0)        # codes 0x01..0x7E increase
+
+
+def test_e4m3_rounding_ties_to_even_and_saturates():
+    enc = W.e4m3_rne_codes
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 3.0: 0x44, 2.0 ** -10: 0x00, 1.5 * 2.0 ** -10: 0x01,
+             2.5 * 2.0 ** -9: 0x02, 3.5 * 2.0 ** -9: 0x04, 7.5 * 2.0 ** -9: 0x08, 464.0: 0x7E,
+             1e6: 0x7E, -2.5: 0xC2, 232.0: 0x76, 0.3: 0x2A}
+    for x, c in cases.items():
+        assert enc(np.array([x]))[0] == c, (x, hex(c))
+    assert enc(np.array([np.nan]))[0] == 0x7F
+
+
+def test_e4m3_round_trip_and_nearest():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = W.e4m3_decode(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(W.e4m3_rne_codes(vals[ok]), codes[ok])
+    # nearest: no finite code is closer than the chosen one
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(2000) * np.exp2(rng.integers(-12, 9, 2000))
+    x = np.clip(x, -448, 448)
+    got = W.e4m3_decode(W.e4m3_rne_codes(x))
+    grid = W.E4M3_VALUES[~np.isnan(W.E4M3_VALUES)]
+    best = np.min(np.abs(x[:, None] - grid[None, :]), axis=1)
+    assert np.all(np.abs(got - x) <= best + 0.0)
+
+
+def test_fp8_workload_is_c3_quantized():
+    w = W.F3.with_(N=256)
+    inp = W.gen_inputs(w)
+    ref = W.gen_inputs(W.C3.with_(N=256, dtype="f32"))
+    for name in ("q", "k", "v"):
+        codes = getattr(inp, name + "_codes")
+        ds = inp.descale[name]
+        assert codes.dtype == np.uint8 and codes.shape == getattr(ref, name).shape
+        # the largest magnitude lands on +-448, and every value is the nearest
+        # e4m3 point of the scaled draw
+        assert np.max(np.abs(W.e4m3_decode(codes))) == 448.0
+        np.testing.assert_array_equal(getattr(inp, name), W.e4m3_decode(codes) * ds)
+        np.testing.assert_array_equal(codes, W.e4m3_rne_codes(getattr(ref, name).astype(np.float64) / ds))

@@ -2,8 +2,8 @@
 
 This module holds no arithmetic of the attention method.  It only draws
 random tensors, rounds them to the storage format the HIP path consumes
-(bf16, round-to-nearest-even, done with integer bit operations), and decodes
-those bits back exactly.  Both sides of every parity check consume the very
+(bf16, round-to-nearest-even, done with integer bit operations; or OCP FP8
+e4m3 codes with a per-tensor scale), and decodes those back exactly.  Both sides of every parity check consume the very
 same bits: the HIP path as bf16 device tensors, the oracle as float64 values
 upcast exactly from them.
 
@@ -14,6 +14,7 @@ Workloads (the pages use random tensors only, so these are the whole inputs):
   C3  bf16, B=1 H=32 Hkv=8 N=8192  d=128, causal,    seed 3, 1% of K rows x8
   C4  bf16, B=1 H=32 Hkv=8 N=32768 d=128, causal,    seed 4, 512 sampled rows
   C5  bf16, B=2 H=16 Hkv=16 N=4096 d=128, causal,    seed 5, backward with dO
+  F3  fp8 (e4m3 codes + per-tensor scales) of C3's draws (seed 3, same outliers)
 
 Draw order inside one generator: q, k, v, then dO (backward workloads only),
 then the outlier key rows (C3 only), then sampled rows (C4 only).  Values are
@@ -60,13 +61,72 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# FP8 storage format: OCP 8-bit floating point, E4M3 variant
+# --------------------------------------------------------------------------
+# Sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+# subnormals m * 2^-9; there are no infinities and S.1111.111 is NaN, so the
+# largest finite magnitude is 1.75 * 2^8 = 448.
+
+def _e4m3_table() -> np.ndarray:
+    t = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            t[c] = np.nan
+            continue
+        v = m * 2.0 ** -9 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        t[c] = -v if c & 0x80 else v
+    return t
+
+
+E4M3_VALUES = _e4m3_table()
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """e4m3 codes (uint8) -> float64 values, exact."""
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_rne_codes(x: np.ndarray) -> np.ndarray:
+    """float64 -> e4m3 codes, round to nearest, ties to even, magnitudes
+    beyond 448 saturate to 448; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, np.minimum(np.abs(x), 2.0 * E4M3_MAX))
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    # subnormal range: multiples of 2^-9 (the count 8 is 2^-6, code 0x08)
+    sub = np.rint(a * 2.0 ** 9).astype(np.int64)
+    f, ex = np.frexp(np.where(a > 0, a, 1.0))         # a = f 2^ex, f in [0.5, 1)
+    e = ex.astype(np.int64) - 1                       # a in [2^e, 2^(e+1))
+    m = np.rint((2.0 * f - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e = e + carry
+    m = np.where(carry, 0, m)
+    normal = ((e + 7) << 3) | m
+    code = np.where(a < 2.0 ** -6, sub, normal)
+    code = np.minimum(code, 0x7E)                     # saturate at 448
+    code = np.where(nan, 0x7F, code | sign)
+    return code.astype(np.uint8)
+
+
+def fp8_quantize(x: np.ndarray) -> tuple[np.ndarray, float]:
+    """Per-tensor scale descale = amax / 448 (rounded to float32) and the
+    e4m3 codes of x / descale; the stored values are descale * e4m3(code)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    return e4m3_rne_codes(np.asarray(x, dtype=np.float64) / descale), descale
+
+
+# --------------------------------------------------------------------------
 # Workload descriptions
 # --------------------------------------------------------------------------
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str  # "f32" or "bf16": the storage type of q, k, v, o (and dO)
+    dtype: str  # "f32", "bf16" or "fp8": the storage type of q, k, v (and o, dO;
+                # fp8 workloads produce a bf16 o)
     B: int
     H: int
     Hkv: int
@@ -117,7 +177,9 @@ C4 = Workload("C4", "bf16", 1, 32, 8, 32768, 128, True, 4,
 C5 = Workload("C5", "bf16", 2, 16, 16, 4096, 128, True, 5, backward=True,
               note="backward with recomputation")
 
-WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
+F3 = replace(C3, name="F3", dtype="fp8")
+
+WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5, F3)}
 
 
 @dataclass
@@ -135,6 +197,12 @@ class Inputs:
     do_bits: np.ndarray | None = None
     outlier_rows: np.ndarray | None = None   # [B, Hkv, n_out] key indices
     sampled_rows: np.ndarray | None = None   # [n, 2] (h, i) pairs, b = 0
+    # fp8 workloads: e4m3 codes and per-tensor scales; q, k, v then hold the
+    # represented values descale * e4m3(code) as float64
+    q_codes: np.ndarray | None = None
+    k_codes: np.ndarray | None = None
+    v_codes: np.ndarray | None = None
+    descale: dict | None = None
 
     def f64(self, name: str) -> np.ndarray:
         return getattr(self, name).astype(np.float64)
@@ -168,6 +236,13 @@ def gen_inputs(w: Workload, seed: int | None = None) -> Inputs:
         sampled = sample_rows(rng, w.H, w.N, w.n_sampled_rows)
 
     inp = Inputs(w, q, k, v, do, outlier_rows=outliers, sampled_rows=sampled)
+    if w.dtype == "fp8":
+        inp.descale = {}
+        for name in ("q", "k", "v"):
+            codes, ds = fp8_quantize(getattr(inp, name))
+            setattr(inp, name + "_codes", codes)
+            inp.descale[name] = ds
+            setattr(inp, name, e4m3_decode(codes) * ds)
     if w.dtype == "bf16":
         # x8 is exact in bf16, so scaling before or after rounding is the same.
         for name in ("q", "k", "v", "do"):
