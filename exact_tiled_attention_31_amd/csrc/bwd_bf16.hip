@@ -109,25 +109,36 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
   const int blk_c = (tid % (D / 8)) * 8;
   const bool loader = tid < T::kBlocks;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * kKT;
-    __syncthreads();
+  // the next tile's K and V rows are loaded into registers while the current
+  // tile is computed, then stored to LDS between two barriers
+  u32x4_t kr[4], vr[4];
+  auto fetch = [&](int k0) {
     if (loader) {
-      u32x4_t kr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kj = k0 + blk_r + r;
         const bool ok = kj < N;
         kr[r] = ok ? *reinterpret_cast<const u32x4_t*>(K + (head_kv + kj) * D + blk_c)
                    : u32x4_t{0, 0, 0, 0};
-        const u32x4_t vr = ok ? *reinterpret_cast<const u32x4_t*>(V + (head_kv + kj) * D + blk_c)
-                              : u32x4_t{0, 0, 0, 0};
+        vr[r] = ok ? *reinterpret_cast<const u32x4_t*>(V + (head_kv + kj) * D + blk_c)
+                   : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  fetch(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kKT;
+    __syncthreads();
+    if (loader) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
         *reinterpret_cast<u32x4_t*>(&sK[(blk_r + r) * T::kRowStride + blk_c]) = kr[r];
-        *reinterpret_cast<u32x4_t*>(&sV[(blk_r + r) * T::kRowStride + blk_c]) = vr;
+        *reinterpret_cast<u32x4_t*>(&sV[(blk_r + r) * T::kRowStride + blk_c]) = vr[r];
       }
       if (MODE == kGrad) store_block_transposed(sKt, T::kTStride, blk_c, blk_r, kr);
     }
     __syncthreads();
+    if (kt + 1 < n_kt) fetch(k0 + kKT);
 
     if (wq_first >= N) continue;
     if (CAUSAL && k0 > wq_last) continue;
@@ -280,22 +291,43 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
   const int blk_c = (tid % (D / 8)) * 8;
   const bool loader = tid < T::kBlocks;
 
-  for (int hh = 0; hh < rep; ++hh) {
-    const int h = g * rep + hh;
-    const size_t head_q = ((size_t)b * H + h) * N;
-    for (int qt = qt_first; qt < n_qt; ++qt) {
-      const int q0 = qt * kQT;
+  // Tiles in order: every query tile that sees the block, for each query head
+  // of the group.  The next tile's Q, dO rows and statistics are loaded into
+  // registers while the current one is computed.
+  const int tiles_per_head = n_qt - qt_first;
+  const int n_tiles = rep * tiles_per_head;
+  u32x4_t qr[4], orow[4];
+  float lpre = 0.f, dpre = 0.f;
+  auto fetch = [&](int t) {
+    const int hh = t / tiles_per_head;
+    const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
+    const size_t head_q = ((size_t)b * H + g * rep + hh) * N;
+    if (loader) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = q0 + blk_r + r;
+        const bool ok = qi < N;
+        qr[r] = ok ? *reinterpret_cast<const u32x4_t*>(Q + (head_q + qi) * D + blk_c)
+                   : u32x4_t{0, 0, 0, 0};
+        orow[r] = ok ? *reinterpret_cast<const u32x4_t*>(dO + (head_q + qi) * D + blk_c)
+                     : u32x4_t{0, 0, 0, 0};
+      }
+    }
+    if (tid < kQT) {
+      const int qi = q0 + tid;
+      lpre = qi < N ? LSE[head_q + qi] * kLog2e : 0.f;
+      dpre = qi < N ? delta[head_q + qi] : 0.f;
+    }
+  };
+  if (n_tiles > 0) fetch(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int hh = t / tiles_per_head;
+    const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
+    {
       __syncthreads();   // previous tile fully consumed
       if (loader) {
-        u32x4_t qr[4], orow[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qi = q0 + blk_r + r;
-          const bool ok = qi < N;
-          qr[r] = ok ? *reinterpret_cast<const u32x4_t*>(Q + (head_q + qi) * D + blk_c)
-                     : u32x4_t{0, 0, 0, 0};
-          orow[r] = ok ? *reinterpret_cast<const u32x4_t*>(dO + (head_q + qi) * D + blk_c)
-                       : u32x4_t{0, 0, 0, 0};
           *reinterpret_cast<u32x4_t*>(&sQ[(blk_r + r) * T::kRowStride + blk_c]) = qr[r];
           *reinterpret_cast<u32x4_t*>(&sO[(blk_r + r) * T::kRowStride + blk_c]) = orow[r];
         }
@@ -303,11 +335,11 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
         store_block_transposed(sOt, T::kTStride, blk_c, blk_r, orow);
       }
       if (tid < kQT) {
-        const int qi = q0 + tid;
-        sL[tid] = qi < N ? LSE[head_q + qi] * kLog2e : 0.f;
-        sD[tid] = qi < N ? delta[head_q + qi] : 0.f;
+        sL[tid] = lpre;
+        sD[tid] = dpre;
       }
       __syncthreads();
+      if (t + 1 < n_tiles) fetch(t + 1);
 
       // this wave's keys kw0..kw0+31 against queries q0..q0+63
       if (kw0 >= N) continue;
