@@ -59,9 +59,10 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
     uint16_t* __restrict__ dQ, int B, int H, int Hkv, int N, float c, float scale,
     int n_qblocks) {
   using T = QTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * T::kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kKT * T::kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[MODE == kGrad ? D * T::kTStride : 8];
+  // double-buffered: tile kt+1 is stored while tile kt is computed
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sKt[2][MODE == kGrad ? D * T::kTStride : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -109,8 +110,9 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
   const int blk_c = (tid % (D / 8)) * 8;
   const bool loader = tid < T::kBlocks;
 
-  // the next tile's K and V rows are loaded into registers while the current
-  // tile is computed, then stored to LDS between two barriers
+  // Tile kt+1's K and V rows, already in registers, are stored into the other
+  // LDS buffer at the start of iteration kt, then tile kt+2 is loaded into the
+  // registers; both overlap tile kt's compute.  One barrier per tile.
   u32x4_t kr[4], vr[4];
   auto fetch = [&](int k0) {
     if (loader) {
@@ -125,23 +127,26 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
       }
     }
   };
-  fetch(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * kKT;
-    __syncthreads();
+  auto stash = [&](int buf) {
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4_t*>(&sK[(blk_r + r) * T::kRowStride + blk_c]) = kr[r];
-        *reinterpret_cast<u32x4_t*>(&sV[(blk_r + r) * T::kRowStride + blk_c]) = vr[r];
+        *reinterpret_cast<u32x4_t*>(&sK[buf][(blk_r + r) * T::kRowStride + blk_c]) = kr[r];
+        *reinterpret_cast<u32x4_t*>(&sV[buf][(blk_r + r) * T::kRowStride + blk_c]) = vr[r];
       }
-      if (MODE == kGrad) store_block_transposed(sKt, T::kTStride, blk_c, blk_r, kr);
+      if (MODE == kGrad) store_block_transposed(sKt[buf], T::kTStride, blk_c, blk_r, kr);
     }
-    __syncthreads();
-    if (kt + 1 < n_kt) fetch(k0 + kKT);
-
-    if (wq_first >= N) continue;
-    if (CAUSAL && k0 > wq_last) continue;
+  };
+  fetch(0);
+  stash(0);
+  if (n_kt > 1) fetch(kKT);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * kKT;
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) stash(buf ^ 1);     // that buffer was last read in iteration kt-1
+    if (kt + 2 < n_kt) fetch(k0 + 2 * kKT);
+    if (wq_first < N && !(CAUSAL && k0 > wq_last)) {
     const bool need_mask = (k0 + kKT > N) || (CAUSAL && k0 + kKT - 1 > wq_first) || !qok;
 
     // S^T = K Q^T, dP^T = V dO^T : two 32-key blocks, lane = query, regs = keys
@@ -152,8 +157,8 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int off = (32 * kb + col) * T::kRowStride + 16 * s + 8 * grp;
-        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(&sK[off]);
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&sV[off]);
+        const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(&sK[buf][off]);
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&sV[buf][off]);
         s_acc[kb] = mfma_32x32x16_bf16(ak, qf[s], s_acc[kb]);
         p_acc[kb] = mfma_32x32x16_bf16(av, of[s], p_acc[kb]);
       }
@@ -189,13 +194,15 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                &sKt[(32 * cb + col) * T::kTStride + 32 * kb + 16 * t + 8 * grp]);
+                &sKt[buf][(32 * cb + col) * T::kTStride + 32 * kb + 16 * t + 8 * grp]);
             dq[cb] = mfma_32x32x16_bf16(a, ds_hi[kb][t], dq[cb]);
             dq[cb] = mfma_32x32x16_bf16(a, ds_lo[kb][t], dq[cb]);
           }
         }
       }
     }
+    }
+    __syncthreads();   // tile kt+1 stored; everyone is done with buffer `buf`
   }
 
   if (MODE == kDelta) {
@@ -241,12 +248,13 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int B, int H, int Hkv, int N, float c, float scale) {
   using T = KVTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kQT * T::kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * T::kTStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[kQT * T::kRowStride];   // dO row-major
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[D * T::kTStride];      // dO^T
-  __shared__ __attribute__((aligned(16))) float sL[kQT];                       // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[kQT];                       // D_i
+  // double-buffered: tile t+1 is stored while tile t is computed
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kQT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][D * T::kTStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kQT * T::kRowStride];   // dO row-major
+  __shared__ __attribute__((aligned(16))) uint16_t sOt[2][D * T::kTStride];      // dO^T
+  __shared__ __attribute__((aligned(16))) float sL[2][kQT];                       // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kQT];                       // D_i
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -292,8 +300,10 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
   const bool loader = tid < T::kBlocks;
 
   // Tiles in order: every query tile that sees the block, for each query head
-  // of the group.  The next tile's Q, dO rows and statistics are loaded into
-  // registers while the current one is computed.
+  // of the group.  Tile t+1's Q, dO rows and statistics, already in registers,
+  // are stored into the other LDS buffer at the start of iteration t, then
+  // tile t+2 is loaded into the registers; both overlap tile t's compute.
+  // One barrier per tile.
   const int tiles_per_head = n_qt - qt_first;
   const int n_tiles = rep * tiles_per_head;
   u32x4_t qr[4], orow[4];
@@ -319,31 +329,36 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
       dpre = qi < N ? delta[head_q + qi] : 0.f;
     }
   };
-  if (n_tiles > 0) fetch(0);
+  auto stash = [&](int buf) {
+    if (loader) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<u32x4_t*>(&sQ[buf][(blk_r + r) * T::kRowStride + blk_c]) = qr[r];
+        *reinterpret_cast<u32x4_t*>(&sO[buf][(blk_r + r) * T::kRowStride + blk_c]) = orow[r];
+      }
+      store_block_transposed(sQt[buf], T::kTStride, blk_c, blk_r, qr);
+      store_block_transposed(sOt[buf], T::kTStride, blk_c, blk_r, orow);
+    }
+    if (tid < kQT) {
+      sL[buf][tid] = lpre;
+      sD[buf][tid] = dpre;
+    }
+  };
+  if (n_tiles > 0) {
+    fetch(0);
+    stash(0);
+    if (n_tiles > 1) fetch(1);
+  }
+  __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
     const int hh = t / tiles_per_head;
     const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
-    {
-      __syncthreads();   // previous tile fully consumed
-      if (loader) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<u32x4_t*>(&sQ[(blk_r + r) * T::kRowStride + blk_c]) = qr[r];
-          *reinterpret_cast<u32x4_t*>(&sO[(blk_r + r) * T::kRowStride + blk_c]) = orow[r];
-        }
-        store_block_transposed(sQt, T::kTStride, blk_c, blk_r, qr);
-        store_block_transposed(sOt, T::kTStride, blk_c, blk_r, orow);
-      }
-      if (tid < kQT) {
-        sL[tid] = lpre;
-        sD[tid] = dpre;
-      }
-      __syncthreads();
-      if (t + 1 < n_tiles) fetch(t + 1);
-
-      // this wave's keys kw0..kw0+31 against queries q0..q0+63
-      if (kw0 >= N) continue;
-      if (CAUSAL && q0 + kQT - 1 < kw0) continue;   // every query precedes every key
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) stash(buf ^ 1);   // that buffer was last read in iteration t-1
+    if (t + 2 < n_tiles) fetch(t + 2);
+    // this wave's keys kw0..kw0+31 against queries q0..q0+63; skipped when every
+    // query precedes every key
+    if (kw0 < N && !(CAUSAL && q0 + kQT - 1 < kw0)) {
       const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31);
 
       // S = Q K^T, dP = dO V^T : two 32-query blocks, lane = key, regs = queries
@@ -354,8 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int off = (32 * qb + col) * T::kRowStride + 16 * s + 8 * grp;
-          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQ[off]);
-          const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sO[off]);
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQ[buf][off]);
+          const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sO[buf][off]);
           s_acc[qb] = mfma_32x32x16_bf16(aq, kf[s], s_acc[qb]);
           p_acc[qb] = mfma_32x32x16_bf16(ao, vf[s], p_acc[qb]);
         }
@@ -368,8 +383,8 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int qq = 32 * qb + 8 * r4 + 4 * grp;    // 4 consecutive query rows
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[qq]);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[qq]);
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][qq]);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][qq]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * r4 + e;
@@ -398,8 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int off = (32 * cb + col) * T::kTStride + 32 * qb + 16 * t + 8 * grp;
-            const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sOt[off]);
-            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQt[off]);
+            const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sOt[buf][off]);
+            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQt[buf][off]);
             dv[cb] = mfma_32x32x16_bf16(ao, p_hi[qb][t], dv[cb]);
             dv[cb] = mfma_32x32x16_bf16(ao, p_lo[qb][t], dv[cb]);
             dk[cb] = mfma_32x32x16_bf16(aq, ds_hi[qb][t], dk[cb]);
@@ -408,6 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
         }
       }
     }
+    __syncthreads();   // tile t+1 stored; everyone is done with buffer `buf`
   }
 
   if (key < N) {
