@@ -18,6 +18,12 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfattn.so")
 SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "bwd_bf16.hip"]
+# Per-source extra flags.  The backward kernels hold more than 256 registers
+# per lane; by default the compiler then gives every matrix-core result an
+# AGPR and copies the score accumulators out for the VALU on every tile.
+# Selecting the VGPR form keeps the scores in VGPRs and lets only the
+# gradient accumulators move to AGPRs.
+SOURCE_FLAGS = {"bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
@@ -57,7 +63,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *flags, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
         p_acc[kb] = mfma_32x32x16_bf16(av, of[s], p_acc[kb]);
       }
     }
+    sched_reads_ahead<4 * T::kKSteps, 1>();
 
     u32x4_t ds_hi[2][2], ds_lo[2][2];
 #pragma unroll
@@ -200,6 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
           }
         }
       }
+      sched_reads_ahead<4 * T::kDBlocks, 2>();
     }
     }
     __syncthreads();   // tile kt+1 stored; everyone is done with buffer `buf`
@@ -375,6 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
           p_acc[qb] = mfma_32x32x16_bf16(ao, vf[s], p_acc[qb]);
         }
       }
+      sched_reads_ahead<4 * T::kKSteps, 1>();
 
       u32x4_t p_hi[2][2], p_lo[2][2], ds_hi[2][2], ds_lo[2][2];
 #pragma unroll
@@ -422,6 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
           }
         }
       }
+      sched_reads_ahead<8 * T::kDBlocks, 2>();
     }
     __syncthreads();   // tile t+1 stored; everyone is done with buffer `buf`
   }

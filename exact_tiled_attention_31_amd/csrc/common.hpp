@@ -131,6 +131,22 @@ __device__ __forceinline__ void store_block_transposed(uint16_t* dst, int stride
   }
 }
 
+// Ask the scheduler to keep LDS operand reads `lead` reads ahead of the
+// matrix-core steps that use them, in a region of `reads` reads that each feed
+// `per` consecutive matrix-core steps.  Without it the reads are issued just
+// before their use and the LDS latency is exposed on every step.
+template <int reads, int per, int lead = 4>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, lead, 0);
+#pragma unroll
+  for (int i = 0; i < reads - lead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, per, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, per * lead, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Buffer unit: global -> LDS copies and range-checked addressing
 // ---------------------------------------------------------------------------
