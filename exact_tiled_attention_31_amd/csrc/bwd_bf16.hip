@@ -25,6 +25,8 @@
 //   3. rows<GRAD>: as 1, then dS^T and dQ^T += K^T dS^T.
 // P and dS enter the matrix cores as hi + lo bf16 pairs (two steps against
 // the same exact bf16 operand), so their rounding stays near fp32.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -146,8 +148,10 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
     const int buf = kt & 1;
     if (kt + 1 < n_kt) stash(buf ^ 1);     // that buffer was last read in iteration kt-1
     if (kt + 2 < n_kt) fetch(k0 + 2 * kKT);
-    if (wq_first < N && !(CAUSAL && k0 > wq_last)) {
-    const bool need_mask = (k0 + kKT > N) || (CAUSAL && k0 + kKT - 1 > wq_first) || !qok;
+    // Two copies of the tile body, with and without masking, so unmasked tiles
+    // carry no per-element compare at all.
+    auto tile_body = [&](auto masked_tag) {
+    constexpr bool need_mask = decltype(masked_tag)::value;
 
     // S^T = K Q^T, dP^T = V dO^T : two 32-key blocks, lane = query, regs = keys
     f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
@@ -165,20 +169,28 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
     }
     sched_reads_ahead<4 * T::kKSteps, 1>();
 
+    float pv[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(fmaf(s_acc[kb][r], c, -l2));
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * grp + (r & 3);
+          if (!qok || (kj >= N) || (CAUSAL && kj > qi)) pv[kb][r] = 0.f;
+        }
+    }
     u32x4_t ds_hi[2][2], ds_lo[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(s_acc[kb][r], c, -l2));
-        if (need_mask) {
-          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * grp + (r & 3);
-          const bool dead = !qok || (kj >= N) || (CAUSAL && kj > qi);
-          if (dead) pv = 0.f;
-        }
-        if (MODE == kDelta) dsum = fmaf(pv, p_acc[kb][r], dsum);
-        else ds[r] = pv * (p_acc[kb][r] - dd);
+        if (MODE == kDelta) dsum = fmaf(pv[kb][r], p_acc[kb][r], dsum);
+        else ds[r] = pv[kb][r] * (p_acc[kb][r] - dd);
       }
       if (MODE == kGrad) {
 #pragma unroll
@@ -203,6 +215,13 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
       }
       sched_reads_ahead<4 * T::kDBlocks, 2>();
     }
+    };
+    if (wq_first < N && !(CAUSAL && k0 > wq_last)) {
+      // !qok: a wave whose rows run past N (all its lanes share one q block)
+      if ((k0 + kKT > N) || (CAUSAL && k0 + kKT - 1 > wq_first) || wq_first + 31 >= N)
+        tile_body(std::true_type{});
+      else
+        tile_body(std::false_type{});
     }
     __syncthreads();   // tile kt+1 stored; everyone is done with buffer `buf`
   }
@@ -360,8 +379,10 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
     if (t + 2 < n_tiles) fetch(t + 2);
     // this wave's keys kw0..kw0+31 against queries q0..q0+63; skipped when every
     // query precedes every key
-    if (kw0 < N && !(CAUSAL && q0 + kQT - 1 < kw0)) {
-      const bool need_mask = (q0 + kQT > N) || (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31);
+    // Two copies of the tile body, with and without masking, so unmasked tiles
+    // carry no per-element compare at all.
+    auto tile_body = [&](auto masked_tag) {
+      constexpr bool need_mask = decltype(masked_tag)::value;
 
       // S = Q K^T, dP = dO V^T : two 32-query blocks, lane = key, regs = queries
       f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
@@ -380,30 +401,40 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
       sched_reads_ahead<4 * T::kKSteps, 1>();
 
       u32x4_t p_hi[2][2], p_lo[2][2], ds_hi[2][2], ds_lo[2][2];
+      float p[2][16];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float p[16], ds[16];
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int qq = 32 * qb + 8 * r4 + 4 * grp;    // 4 consecutive query rows
           const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][qq]);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][qq]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            float pv = fast_exp2(fmaf(s_acc[qb][r], c, -l4[e]));
-            if (need_mask) {
-              const int qi = q0 + qq + e;
-              const bool dead = (qi >= N) || (key >= N) || (CAUSAL && key > qi);
-              if (dead) pv = 0.f;
-            }
-            p[r] = pv;
-            ds[r] = pv * (p_acc[qb][r] - d4[e]);
+          for (int e = 0; e < 4; ++e)
+            p[qb][4 * r4 + e] = fast_exp2(fmaf(s_acc[qb][4 * r4 + e], c, -l4[e]));
+        }
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * grp + (r & 3);
+            if ((qi >= N) || (key >= N) || (CAUSAL && key > qi)) p[qb][r] = 0.f;
           }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t d4 =
+              *reinterpret_cast<const f32x4_t*>(&sD[buf][32 * qb + 8 * r4 + 4 * grp]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ds[4 * r4 + e] = p[qb][4 * r4 + e] * (p_acc[qb][4 * r4 + e] - d4[e]);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          split_bf16x8(&p[8 * t], p_hi[qb][t], p_lo[qb][t]);
+          split_bf16x8(&p[qb][8 * t], p_hi[qb][t], p_lo[qb][t]);
           split_bf16x8(&ds[8 * t], ds_hi[qb][t], ds_lo[qb][t]);
         }
       }
@@ -426,6 +457,12 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
         }
       }
       sched_reads_ahead<8 * T::kDBlocks, 2>();
+    };
+    if (kw0 < N && !(CAUSAL && q0 + kQT - 1 < kw0)) {
+      if ((q0 + kQT > N) || (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31))
+        tile_body(std::true_type{});
+      else
+        tile_body(std::false_type{});
     }
     __syncthreads();   // tile t+1 stored; everyone is done with buffer `buf`
   }
