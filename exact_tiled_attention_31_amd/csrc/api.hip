@@ -11,8 +11,8 @@ namespace {
 
 constexpr long double kMaxElems = 4611686018427387904.0L;   // 2^62
 constexpr long long kMaxRows = 2147483647LL;                // 2^31 - 1
-// The bf16 forward addresses one head's K and V through a buffer resource
-// with a 32-bit byte range and 32-bit offsets.
+// The bf16 and fp8 forwards address one head's K and V through a buffer
+// resource with a 32-bit byte range and 32-bit offsets.
 constexpr long long kMaxHeadBytes = 2147483647LL;           // 2^31 - 1
 
 struct Range {
@@ -48,7 +48,7 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
   int st = check_sizes(B, H, Hkv, N, d, empty);
   if (st != FA_OK || *empty) return st;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (elem == 2 && (long long)N * d * 2 > kMaxHeadBytes) return FA_ERR_INVALID_ARG;
+  if (elem <= 2 && (long long)N * d * (long long)elem > kMaxHeadBytes) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4))

@@ -38,9 +38,9 @@
  *                         H % Hkv != 0, non-finite scale, a pointer not aligned
  *                         to 16 bytes (4 for lse), an output overlapping an
  *                         input, sizes whose index space exceeds 2^62 or
- *                         whose row count B*H*N exceeds 2^31 - 1, or (fa_fwd
- *                         only) one head's K or V slab of N*d*2 bytes
- *                         exceeding 2^31 - 1;
+ *                         whose row count B*H*N exceeds 2^31 - 1, or (the bf16
+ *                         and fp8 forwards) one head's K or V slab of N*d
+ *                         elements exceeding 2^31 - 1 bytes;
  *     FA_ERR_UNSUPPORTED  a head dimension other than 64 or 128;
  *     FA_ERR_HIP          the HIP runtime refused the launch.
  * B == 0 or N == 0 is an empty problem: FA_OK, nothing is read, written or

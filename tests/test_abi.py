@@ -128,6 +128,7 @@ def test_fp8_validation():
                {"q": ctypes.c_void_p(A + 8)}):
         assert f8(**kw) == INV, kw
     assert f8(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert f8(H=1, Hkv=1, N=1 << 24, d=128) == INV        # K slab of 2^31 bytes
     assert f8(N=0, q=None, dq=0.0) == fa.FA_OK              # empty problem first
 
 
