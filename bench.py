@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_31_amd", "csrc", f)
@@ -179,6 +180,37 @@ def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps):
             "steps": steps}
 
 
+def short_n_sweep(fa, W, torch, np, dev, stream, warmup, steps):
+    """Informational: the headline head layout (B=1, 32 query heads on 8 kv
+    heads, d=128, bf16, causal) at decode-like short sequence lengths.  These
+    launches are far too small to be compute-bound; the rate reported is the
+    compulsory HBM traffic (Q, K, V read once, O and LSE written once) per
+    kernel duration (HIP events), against the 8 TB/s HBM peak."""
+    out = []
+    for n in (128, 256, 512, 1024):
+        w = W.C3.with_(N=n, outlier_frac=0.0)
+        inp = W.gen_inputs(w)
+        q, k, v = (torch.from_numpy(getattr(inp, x + "_bits").view(np.int16)).view(torch.bfloat16)
+                   .to(dev) for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(steps):
+            fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        gbs = w.compulsory_bytes() / (ms * 1e-3) / 1e9
+        out.append({"N": n, "us": round(ms * 1e3, 2), "compulsory_bytes": w.compulsory_bytes(),
+                    "GB_per_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +221,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")
+    ap.add_argument("--no-short-n", action="store_true",
+                    help="skip the informational short-sequence sweep (N = 128 .. 1024)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the informational FP8 forward timing")
     ap.add_argument("--no-local", action="store_true",
@@ -277,6 +311,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
     }
+    if not args.no_short_n:
+        out["short_n"] = short_n_sweep(fa, W, torch, np, dev, stream, args.warmup, args.steps)
     if not args.no_fp8:
         out["fp8"] = fp8_timing(fa, W, torch, np, dev, stream, args.warmup, args.steps)
     if not args.no_local:
