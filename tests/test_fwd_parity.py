@@ -234,3 +234,21 @@ def test_empty_problem_is_a_noop():
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
     o, lse = fa.fa_fwd(q, q[:, :1], q[:, :1], causal=True)
     assert o.shape == (1, 2, 0, 128) and lse.shape == (1, 2, 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_keys_force_many_rebases(causal):
+    # Key rows scaled by 1 + j/16 make the scores of later keys grow far past
+    # the reference taken on the first tile (hundreds of log2 units by the end
+    # of the sequence), so the reference is raised and O, l rebased on many
+    # tiles; d=128 and d=64, bf16 (exact scaling up to rounding of the products,
+    # applied to the float draws before the bf16 rounding).
+    torch, fa = require_gpu()
+    for d, seed in ((128, 161), (64, 162)):
+        w = W.small_case(f"growing_keys_d{d}", "bf16", 1, 4, 2, 1000, d, causal, seed)
+        inp = W.gen_inputs(w)
+        grow = (1.0 + np.arange(w.N, dtype=np.float32) / 16.0)[None, None, :, None]
+        inp.k_bits = W.bf16_rne_bits(W.bf16_bits_to_f32(inp.k_bits) * grow)
+        inp.k = W.bf16_bits_to_f32(inp.k_bits)
+        o, lse = run_fwd(inp, fa, torch)
+        compare_full(inp, o, lse, causal, w.scale, f"growing keys d={d} causal={causal}")

@@ -104,3 +104,19 @@ def test_deterministic():
     o2, l2 = fa.fa_fwd_local(q, k, v, 300, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_growing_keys_force_many_rebases():
+    # as in the full-attention test: later keys' scores grow far past the
+    # reference taken on a row's first visible tile
+    torch, fa = require_gpu()
+    w = W.small_case("local_growing", "bf16", 1, 4, 2, 1000, 128, True, 214)
+    inp = W.gen_inputs(w)
+    grow = (1.0 + np.arange(w.N, dtype=np.float32) / 16.0)[None, None, :, None]
+    inp.k_bits = W.bf16_rne_bits(W.bf16_bits_to_f32(inp.k_bits) * grow)
+    inp.k = W.bf16_bits_to_f32(inp.k_bits)
+    for window in (70, 300):
+        o, lse = run_local(inp, fa, torch, window)
+        O, L = oracle.attention_fwd(inp.q, inp.k, inp.v, True, w.scale, window=window)
+        check_bf16(dev_bf16_to_f64(o), O, f"local growing w={window}")
+        check_lse(dev_to_f64(lse), L, f"local growing w={window}")
