@@ -92,11 +92,10 @@ template <int D, bool CAUSAL, bool LOCAL, int WAVES, int BLOCKS>
 __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks, int window) {
+    int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks, int window, int hp) {
   static_assert(CAUSAL || !LOCAL, "local attention is causal");
   using T = Tile<D>;
   constexpr int kRowsPerWave = 32 * BLOCKS;
-  constexpr int kBM = WAVES * kRowsPerWave;
   // [buffer][K tile | V tile]
   constexpr int kStage = T::kKTile + T::kVTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
@@ -107,23 +106,31 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   const int col = lane & 31;
   const int grp = lane >> 5;
 
-  // ---- work item: heavy causal query blocks first --------------------------
-  const int BH = B * H;
-  const int item_q = blockIdx.x / BH;
-  const int bh = blockIdx.x - item_q * BH;
+  // ---- work item: hp query heads that share one kv head, the same block of
+  // rows_h query rows in each; heavy causal query blocks first.  All waves of
+  // the workgroup then see the same causal extent, and one K/V tile serves
+  // every head of the group.
+  const int wph = WAVES / hp;                    // waves per query head
+  const int rows_h = wph * kRowsPerWave;         // query rows per head
+  const int rep = H / Hkv;
+  const int n_groups = B * Hkv * (rep / hp);
+  const int item_q = blockIdx.x / n_groups;
+  const int grp_id = blockIdx.x - item_q * n_groups;
   const int qb = CAUSAL ? (n_qblocks - 1 - item_q) : item_q;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const int g = h / (H / Hkv);
-  const int q0 = qb * kBM;
+  const int bg = grp_id / (rep / hp);
+  const int hs = grp_id - bg * (rep / hp);
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
+  const int h = g * rep + hs * hp + wave / wph;  // this wave's query head
+  const int q0 = qb * rows_h;
 
-  const size_t head_q = (size_t)bh * N;
+  const size_t head_q = ((size_t)b * H + h) * N;
   const size_t head_kv = ((size_t)b * Hkv + g) * N;
   const uint16_t* Qh = Q + head_q * D;
   const i32x4_t k_rsrc = make_buffer_rsrc(K + head_kv * D, (uint32_t)N * T::kRowBytes);
   const i32x4_t v_rsrc = make_buffer_rsrc(V + head_kv * D, (uint32_t)N * T::kRowBytes);
 
-  const int wq_first = q0 + wave * kRowsPerWave;   // this wave's first query row
+  const int wq_first = q0 + (wave % wph) * kRowsPerWave;   // this wave's first query row
   int qi[BLOCKS];
 #pragma unroll
   for (int hf = 0; hf < BLOCKS; ++hf) qi[hf] = wq_first + 32 * hf + col;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
     }
   }
 
-  const int q_hi = min(q0 + kBM, N);
+  const int q_hi = min(q0 + rows_h, N);
   int n_kt = (N + kBN - 1) / kBN;
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kBN + 1);
   // first tile holding a key that the block's first query still sees
@@ -403,9 +410,13 @@ constexpr int kBlocks = FATTN_FWD_BLOCKS;
 
 template <int D, bool CAUSAL, bool LOCAL>
 hipError_t launch_one(const FwdArgs& a) {
-  constexpr int kBM = kWaves * 32 * kBlocks;
-  const int n_qblocks = (a.N + kBM - 1) / kBM;
-  const long long items = (long long)n_qblocks * a.B * a.H;
+  // query heads per workgroup: as many of a kv head's query heads as divide
+  // both the group size and the wave count (at most 4, so a head keeps 64 rows)
+  const int rep = a.H / a.Hkv;
+  const int hp = (rep % 4 == 0 && kWaves % 4 == 0) ? 4 : (rep % 2 == 0 && kWaves % 2 == 0) ? 2 : 1;
+  const int rows_h = (kWaves / hp) * 32 * kBlocks;
+  const int n_qblocks = (a.N + rows_h - 1) / rows_h;
+  const long long items = (long long)n_qblocks * a.B * a.H / hp;
   // c > 0 lets masked scores (-inf) give exp2(-inf) = 0 directly; for scale 0
   // a c of 1e-30 changes no weight (|s| c stays far below fp32 resolution).
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
@@ -414,7 +425,7 @@ hipError_t launch_one(const FwdArgs& a) {
                        dim3((unsigned)items), dim3(64 * kWaves), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
-                       a.B, a.H, a.Hkv, a.N, c, neg_q, n_qblocks, a.window);
+                       a.B, a.H, a.Hkv, a.N, c, neg_q, n_qblocks, a.window, hp);
 }
 
 }  // namespace
