@@ -35,7 +35,6 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
-PEAK_HBM_GBS = 8000.0         # MI355X HBM3E (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_31_amd", "csrc", f)
                for f in ("fwd_bf16.hip", "common.hpp")]
