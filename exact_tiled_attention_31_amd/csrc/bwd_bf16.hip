@@ -35,6 +35,74 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Staging tiles of the backward and their bank layout.  Measured on gfx950:
+// LDS writes are served 128 bytes per cycle with 32-bank conflicts (16-byte
+// stores in phases of 8 consecutive lanes, 8-byte stores in phases of 16
+// lanes); 16-byte reads are served 256 bytes per cycle over 64 banks, a phase
+// pairing lanes 0-7 with 24-31 and 8-15 with 16-23 (likewise in the upper
+// half-wave).
+//
+// A loader thread holds a 4-row x 8-column block: rows 4*kg .. 4*kg+3,
+// columns 8*ch .. 8*ch+7.  Loader index bits 0..3 carry (kg bit 2, ch bit 1,
+// ch bit 2, kg bit 1), bit 4 ch bit 0; the rest carry ch bit 3 (D = 128) and
+// kg bits 0 and 3.  Together with two XOR swizzles this makes every store and
+// every operand read below conflict-free:
+//   * row-major tiles (rows padded by 16 bytes): 16-byte chunk c of row r is
+//     stored at chunk c ^ (((r >> 3) ^ (r >> 4)) & 1);
+//   * transposed (d-major) tiles: logical position p of row d is stored at
+//     p ^ (8 * (((d >> 3) ^ (d >> 4)) & 1) + 32 * ((d >> 5) & 1)).
+template <int D>
+__device__ __forceinline__ int loader_kg(int t) {
+  const int kg1 = (t >> 3) & 1, kg2 = t & 1;
+  const int kg0 = D == 128 ? (t >> 6) & 1 : (t >> 5) & 1;
+  const int kg3 = D == 128 ? (t >> 7) & 1 : (t >> 6) & 1;
+  return kg0 | (kg1 << 1) | (kg2 << 2) | (kg3 << 3);
+}
+template <int D>
+__device__ __forceinline__ int loader_chunk(int t) {
+  const int ch3 = D == 128 ? (t >> 5) & 1 : 0;
+  return ((t >> 4) & 1) | (((t >> 1) & 1) << 1) | (((t >> 2) & 1) << 2) | (ch3 << 3);
+}
+static_assert(kThreads == 256, "loader layout assumes 256 threads");
+
+// Element column where row `row`'s columns c0 .. c0+7 (c0 a multiple of 8) live.
+__device__ __forceinline__ int rm_swz(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
+__device__ __forceinline__ int rm_col(int row, int c0) { return c0 ^ (8 * rm_swz(row)); }
+// Element offset of columns 16*s + 8*grp .. +7 of row-major row 32*rb + col.
+__device__ __forceinline__ int rm_read_off(int stride, int rb, int col, int s, int grp) {
+  return (32 * rb + col) * stride + 16 * s + 8 * (grp ^ rm_swz(col));
+}
+__device__ __forceinline__ int tr_swz(int d) {
+  return 8 * (((d >> 3) ^ (d >> 4)) & 1) + 32 * ((d >> 5) & 1);
+}
+
+// Store rows r0..r0+3 (four 16-byte row segments, columns c0..c0+7) into a
+// swizzled transposed tile: column c0+i, logical positions tr_pos(r0)..+3.
+__device__ __forceinline__ void store_block_transposed_swz(uint16_t* dst, int stride, int c0,
+                                                           int r0, const u32x4_t (&rows)[4]) {
+  const int pos0 = tr_pos(r0) ^ tr_swz(c0);   // c0 is a multiple of 8: same for c0..c0+7
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int w = i >> 1;
+    u32x2_t pair;
+    if ((i & 1) == 0) {
+      pair.x = pack_lo_halves(rows[0][w], rows[1][w]);
+      pair.y = pack_lo_halves(rows[2][w], rows[3][w]);
+    } else {
+      pair.x = pack_hi_halves(rows[0][w], rows[1][w]);
+      pair.y = pack_hi_halves(rows[2][w], rows[3][w]);
+    }
+    *reinterpret_cast<u32x2_t*>(&dst[(c0 + i) * stride + pos0]) = pair;
+  }
+}
+
+// Element offset of logical positions 32*hb + 16*t + 8*grp .. +7 of
+// transposed row 32*cb + col in a swizzled tile.
+__device__ __forceinline__ int tr_read_off(int stride, int cb, int col, int hb, int t, int grp) {
+  return (32 * cb + col) * stride + 32 * (hb ^ (cb & 1)) + 16 * t +
+         8 * (grp ^ (((col >> 3) ^ (col >> 4)) & 1));
+}
+
 // ---------------------------------------------------------------------------
 // Query-block stationary kernel: D (DELTA) or dQ (GRAD)
 // ---------------------------------------------------------------------------
@@ -108,8 +176,11 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kKT + 1);
   const int wq_first = q0 + 32 * wave;
   const int wq_last = wq_first + 31;
-  const int blk_r = (tid / (D / 8)) * 4;
-  const int blk_c = (tid % (D / 8)) * 8;
+  // The D pass has no transposed tile: a plain layout (column chunk fastest,
+  // no swizzle) keeps its row-major stores and reads conflict-free.
+  constexpr bool kSwz = MODE == kGrad;
+  const int blk_r = kSwz ? 4 * loader_kg<D>(tid) : 4 * (tid / (D / 8));
+  const int blk_c = kSwz ? 8 * loader_chunk<D>(tid) : 8 * (tid % (D / 8));
   const bool loader = tid < T::kBlocks;
 
   // Tile kt+1's K and V rows, already in registers, are stored into the other
@@ -133,10 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4_t*>(&sK[buf][(blk_r + r) * T::kRowStride + blk_c]) = kr[r];
-        *reinterpret_cast<u32x4_t*>(&sV[buf][(blk_r + r) * T::kRowStride + blk_c]) = vr[r];
+        const int at = (blk_r + r) * T::kRowStride + (kSwz ? rm_col(blk_r, blk_c) : blk_c);
+        *reinterpret_cast<u32x4_t*>(&sK[buf][at]) = kr[r];
+        *reinterpret_cast<u32x4_t*>(&sV[buf][at]) = vr[r];
       }
-      if (MODE == kGrad) store_block_transposed(sKt[buf], T::kTStride, blk_c, blk_r, kr);
+      if (MODE == kGrad) store_block_transposed_swz(sKt[buf], T::kTStride, blk_c, blk_r, kr);
     }
   };
   fetch(0);
@@ -160,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
     for (int s = 0; s < T::kKSteps; ++s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int off = (32 * kb + col) * T::kRowStride + 16 * s + 8 * grp;
+        const int off = kSwz ? rm_read_off(T::kRowStride, kb, col, s, grp)
+                             : (32 * kb + col) * T::kRowStride + 16 * s + 8 * grp;
         const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(&sK[buf][off]);
         const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&sV[buf][off]);
         s_acc[kb] = mfma_32x32x16_bf16(ak, qf[s], s_acc[kb]);
@@ -207,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void rows_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                &sKt[buf][(32 * cb + col) * T::kTStride + 32 * kb + 16 * t + 8 * grp]);
+                &sKt[buf][tr_read_off(T::kTStride, cb, col, kb, t, grp)]);
             dq[cb] = mfma_32x32x16_bf16(a, ds_hi[kb][t], dq[cb]);
             dq[cb] = mfma_32x32x16_bf16(a, ds_lo[kb][t], dq[cb]);
           }
@@ -316,8 +389,8 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
 
   const int qt_first = CAUSAL ? (k0 / kQT) : 0;
   const int n_qt = (N + kQT - 1) / kQT;
-  const int blk_r = (tid / (D / 8)) * 4;    // loader: 4 rows x 8 columns per thread
-  const int blk_c = (tid % (D / 8)) * 8;
+  const int blk_r = 4 * loader_kg<D>(tid);    // loader: 4 rows x 8 columns per thread
+  const int blk_c = 8 * loader_chunk<D>(tid);
   const bool loader = tid < T::kBlocks;
 
   // Tiles in order: every query tile that sees the block, for each query head
@@ -354,11 +427,12 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4_t*>(&sQ[buf][(blk_r + r) * T::kRowStride + blk_c]) = qr[r];
-        *reinterpret_cast<u32x4_t*>(&sO[buf][(blk_r + r) * T::kRowStride + blk_c]) = orow[r];
+        const int at = (blk_r + r) * T::kRowStride + rm_col(blk_r, blk_c);
+        *reinterpret_cast<u32x4_t*>(&sQ[buf][at]) = qr[r];
+        *reinterpret_cast<u32x4_t*>(&sO[buf][at]) = orow[r];
       }
-      store_block_transposed(sQt[buf], T::kTStride, blk_c, blk_r, qr);
-      store_block_transposed(sOt[buf], T::kTStride, blk_c, blk_r, orow);
+      store_block_transposed_swz(sQt[buf], T::kTStride, blk_c, blk_r, qr);
+      store_block_transposed_swz(sOt[buf], T::kTStride, blk_c, blk_r, orow);
     }
     if (tid < kQT) {
       sL[buf][tid] = lpre;
@@ -391,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
       for (int s = 0; s < T::kKSteps; ++s) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const int off = (32 * qb + col) * T::kRowStride + 16 * s + 8 * grp;
+          const int off = rm_read_off(T::kRowStride, qb, col, s, grp);
           const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQ[buf][off]);
           const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sO[buf][off]);
           s_acc[qb] = mfma_32x32x16_bf16(aq, kf[s], s_acc[qb]);
@@ -446,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
         for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int off = (32 * cb + col) * T::kTStride + 32 * qb + 16 * t + 8 * grp;
+            const int off = tr_read_off(T::kTStride, cb, col, qb, t, grp);
             const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sOt[buf][off]);
             const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQt[buf][off]);
             dv[cb] = mfma_32x32x16_bf16(ao, p_hi[qb][t], dv[cb]);
