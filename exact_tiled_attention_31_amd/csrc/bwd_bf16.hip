@@ -37,24 +37,25 @@ constexpr int kThreads = 256;
 
 // Staging tiles of the backward and their bank layout.  Measured on gfx950:
 // LDS writes are served 128 bytes per cycle with 32-bank conflicts (16-byte
-// stores in phases of 8 consecutive lanes, 8-byte stores in phases of 16
-// lanes); 16-byte reads are served 256 bytes per cycle over 64 banks, a phase
-// pairing lanes 0-7 with 24-31 and 8-15 with 16-23 (likewise in the upper
-// half-wave).
+// stores in phases of 8 consecutive lanes, 8-byte stores in phases of 16);
+// 16-byte reads are served 256 bytes per cycle over 64 banks, one phase being
+// the 4-lane quads of a half-wave whose quad indices (lane bits 2-4) have the
+// same parity.
 //
 // A loader thread holds a 4-row x 8-column block: rows 4*kg .. 4*kg+3,
-// columns 8*ch .. 8*ch+7.  Loader index bits 0..3 carry (kg bit 2, ch bit 1,
+// columns 8*ch .. 8*ch+7.  Loader index bits 0..3 carry (kg bit 0, ch bit 1,
 // ch bit 2, kg bit 1), bit 4 ch bit 0; the rest carry ch bit 3 (D = 128) and
-// kg bits 0 and 3.  Together with two XOR swizzles this makes every store and
-// every operand read below conflict-free:
+// kg bits 2 and 3.  With two XOR swizzles that are constant over every read
+// phase, every store and every operand read below is conflict-free:
 //   * row-major tiles (rows padded by 16 bytes): 16-byte chunk c of row r is
-//     stored at chunk c ^ (((r >> 3) ^ (r >> 4)) & 1);
+//     stored at chunk c ^ parity(r bits 2..4);
 //   * transposed (d-major) tiles: logical position p of row d is stored at
-//     p ^ (8 * (((d >> 3) ^ (d >> 4)) & 1) + 32 * ((d >> 5) & 1)).
+//     p ^ (16 * parity(d bits 2..4) + 32 * (d bit 5)).
+__device__ __forceinline__ int parity3(int x) { return __builtin_popcount(x & 7) & 1; }
 template <int D>
 __device__ __forceinline__ int loader_kg(int t) {
-  const int kg1 = (t >> 3) & 1, kg2 = t & 1;
-  const int kg0 = D == 128 ? (t >> 6) & 1 : (t >> 5) & 1;
+  const int kg0 = t & 1, kg1 = (t >> 3) & 1;
+  const int kg2 = D == 128 ? (t >> 6) & 1 : (t >> 5) & 1;
   const int kg3 = D == 128 ? (t >> 7) & 1 : (t >> 6) & 1;
   return kg0 | (kg1 << 1) | (kg2 << 2) | (kg3 << 3);
 }
@@ -65,22 +66,21 @@ __device__ __forceinline__ int loader_chunk(int t) {
 }
 static_assert(kThreads == 256, "loader layout assumes 256 threads");
 
+__device__ __forceinline__ int rm_swz(int row) { return parity3(row >> 2); }
 // Element column where row `row`'s columns c0 .. c0+7 (c0 a multiple of 8) live.
-__device__ __forceinline__ int rm_swz(int row) { return ((row >> 3) ^ (row >> 4)) & 1; }
 __device__ __forceinline__ int rm_col(int row, int c0) { return c0 ^ (8 * rm_swz(row)); }
 // Element offset of columns 16*s + 8*grp .. +7 of row-major row 32*rb + col.
 __device__ __forceinline__ int rm_read_off(int stride, int rb, int col, int s, int grp) {
   return (32 * rb + col) * stride + 16 * s + 8 * (grp ^ rm_swz(col));
 }
-__device__ __forceinline__ int tr_swz(int d) {
-  return 8 * (((d >> 3) ^ (d >> 4)) & 1) + 32 * ((d >> 5) & 1);
-}
+__device__ __forceinline__ int tr_swz(int d) { return 16 * parity3(d >> 2) + 32 * ((d >> 5) & 1); }
 
 // Store rows r0..r0+3 (four 16-byte row segments, columns c0..c0+7) into a
 // swizzled transposed tile: column c0+i, logical positions tr_pos(r0)..+3.
 __device__ __forceinline__ void store_block_transposed_swz(uint16_t* dst, int stride, int c0,
                                                            int r0, const u32x4_t (&rows)[4]) {
-  const int pos0 = tr_pos(r0) ^ tr_swz(c0);   // c0 is a multiple of 8: same for c0..c0+7
+  // c0 is a multiple of 8, so the swizzle of column c0+i is tr_swz(c0) ^ 16*(i >> 2)
+  const int pos0 = tr_pos(r0) ^ tr_swz(c0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int w = i >> 1;
@@ -92,15 +92,14 @@ __device__ __forceinline__ void store_block_transposed_swz(uint16_t* dst, int st
       pair.x = pack_hi_halves(rows[0][w], rows[1][w]);
       pair.y = pack_hi_halves(rows[2][w], rows[3][w]);
     }
-    *reinterpret_cast<u32x2_t*>(&dst[(c0 + i) * stride + pos0]) = pair;
+    *reinterpret_cast<u32x2_t*>(&dst[(c0 + i) * stride + (pos0 ^ (16 * (i >> 2)))]) = pair;
   }
 }
 
 // Element offset of logical positions 32*hb + 16*t + 8*grp .. +7 of
 // transposed row 32*cb + col in a swizzled tile.
 __device__ __forceinline__ int tr_read_off(int stride, int cb, int col, int hb, int t, int grp) {
-  return (32 * cb + col) * stride + 32 * (hb ^ (cb & 1)) + 16 * t +
-         8 * (grp ^ (((col >> 3) ^ (col >> 4)) & 1));
+  return (32 * cb + col) * stride + 32 * (hb ^ (cb & 1)) + 16 * (t ^ parity3(col >> 2)) + 8 * grp;
 }
 
 // ---------------------------------------------------------------------------
