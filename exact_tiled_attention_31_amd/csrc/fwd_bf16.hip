@@ -89,7 +89,7 @@ __device__ __forceinline__ void interleave_reads_and_mfma() {
 // LOCAL (which implies CAUSAL): query i sees keys i - window + 1 .. i only;
 // key tiles older than every row of the workgroup are never loaded.
 template <int D, bool CAUSAL, bool LOCAL, int WAVES, int BLOCKS>
-__global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks, int window, int hp) {
@@ -398,34 +398,47 @@ __global__ __launch_bounds__(64 * WAVES, 1) void fwd_bf16_kernel(
   }
 }
 
-// Workgroup shape: waves per workgroup and 32-row blocks per wave.
-#ifndef FATTN_FWD_WAVES
-#define FATTN_FWD_WAVES 8
-#endif
-#ifndef FATTN_FWD_BLOCKS
-#define FATTN_FWD_BLOCKS 1
-#endif
-constexpr int kWaves = FATTN_FWD_WAVES;
-constexpr int kBlocks = FATTN_FWD_BLOCKS;
+// Workgroup shape: 8 waves (two per SIMD) of one 32-row block each.  Short
+// sequences, whose 8-wave grid would leave CUs idle, use 4-wave workgroups
+// (two per CU) instead: twice the workgroups, half the rows on each one's
+// serial chain of key tiles.
+constexpr int kBlocks = 1;
 
-template <int D, bool CAUSAL, bool LOCAL>
-hipError_t launch_one(const FwdArgs& a) {
+template <int WAVES>
+long long grid_items(const FwdArgs& a, int* hp_out, int* n_qblocks_out) {
   // query heads per workgroup: as many of a kv head's query heads as divide
-  // both the group size and the wave count (at most 4, so a head keeps 64 rows)
+  // both the group size and the wave count (at most 4)
   const int rep = a.H / a.Hkv;
-  const int hp = (rep % 4 == 0 && kWaves % 4 == 0) ? 4 : (rep % 2 == 0 && kWaves % 2 == 0) ? 2 : 1;
-  const int rows_h = (kWaves / hp) * 32 * kBlocks;
+  const int hp = (rep % 4 == 0 && WAVES % 4 == 0) ? 4 : (rep % 2 == 0 && WAVES % 2 == 0) ? 2 : 1;
+  const int rows_h = (WAVES / hp) * 32 * kBlocks;
   const int n_qblocks = (a.N + rows_h - 1) / rows_h;
-  const long long items = (long long)n_qblocks * a.B * a.H / hp;
+  *hp_out = hp;
+  *n_qblocks_out = n_qblocks;
+  return (long long)n_qblocks * a.B * a.H / hp;
+}
+
+template <int D, bool CAUSAL, bool LOCAL, int WAVES>
+hipError_t launch_shape(const FwdArgs& a) {
+  int hp = 1, n_qblocks = 0;
+  const long long items = grid_items<WAVES>(a, &hp, &n_qblocks);
   // c > 0 lets masked scores (-inf) give exp2(-inf) = 0 directly; for scale 0
   // a c of 1e-30 changes no weight (|s| c stays far below fp32 resolution).
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int neg_q = a.scale < 0.f ? 1 : 0;
-  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, LOCAL, kWaves, kBlocks>,
-                       dim3((unsigned)items), dim3(64 * kWaves), 0, a.stream,
+  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, LOCAL, WAVES, kBlocks>,
+                       dim3((unsigned)items), dim3(64 * WAVES), 0, a.stream,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                        a.B, a.H, a.Hkv, a.N, c, neg_q, n_qblocks, a.window, hp);
+}
+
+constexpr long long kSmallGrid = 2 * 256;   // 8-wave workgroups: fewer than two per CU
+
+template <int D, bool CAUSAL, bool LOCAL>
+hipError_t launch_one(const FwdArgs& a) {
+  int hp = 1, n_qblocks = 0;
+  if (grid_items<8>(a, &hp, &n_qblocks) < kSmallGrid) return launch_shape<D, CAUSAL, LOCAL, 4>(a);
+  return launch_shape<D, CAUSAL, LOCAL, 8>(a);
 }
 
 }  // namespace
