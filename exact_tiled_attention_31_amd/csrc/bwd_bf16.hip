@@ -120,8 +120,11 @@ struct QTile {
   static_assert(kBlocks <= kThreads, "one block per thread at most");
 };
 
+// The D pass fits two workgroups per CU (LDS and at most 256 registers per
+// lane), so two waves share each SIMD and hide each other's latency; the dQ
+// pass needs more registers and runs one wave per SIMD.
 template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void rows_kernel(
+__global__ __launch_bounds__(kThreads, MODE == kDelta ? 2 : 1) void rows_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, float* __restrict__ delta,
