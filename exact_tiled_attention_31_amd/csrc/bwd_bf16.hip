@@ -11,8 +11,8 @@
 //     dV_j = sum_i P_ij dO_i,   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
 //
 // Three kernels, no atomics (deterministic):
-//   1. rows<DELTA>: one workgroup per (batch, query head, 128-query block),
-//      lane = query; walks the visible key tiles computing S^T = K Q^T and
+//   1. rows<DELTA>: one 4-wave workgroup per (batch, query head, 128-query
+//      block), lane = query; walks the visible key tiles computing S^T = K Q^T and
 //      dP^T = V dO^T and sums D_i = sum_j P_ij dP_ij in fp32.  D is taken
 //      from the recomputed P and dP rather than from the bf16-rounded O, whose
 //      rounding would otherwise dominate the gradient error.
@@ -22,7 +22,11 @@
 //      every 64-query tile that sees the block: S = Q K^T, P, dP = dO V^T,
 //      dS, dV^T += dO^T P, dK^T += Q^T dS.  Q and dO are staged in LDS
 //      row-major and transposed.
-//   3. rows<GRAD>: as 1, then dS^T and dQ^T += K^T dS^T.
+//   3. rows<GRAD>: as 1 with 8-wave workgroups (256 queries), then dS^T and
+//      dQ^T += K^T dS^T.
+// The rows kernels take each 64-key tile as two 32-key halves, one after the
+// other, so only one half's scores, dP and dS are live: both then fit two
+// waves per SIMD (at most 256 registers per lane).
 // P and dS enter the matrix cores as hi + lo bf16 pairs (two steps against
 // the same exact bf16 operand), so their rounding stays near fp32.
 #include <type_traits>
@@ -105,8 +109,9 @@ __device__ __forceinline__ int tr_read_off(int stride, int cb, int col, int hb, 
 // ---------------------------------------------------------------------------
 // Query-block stationary kernel: D (DELTA) or dQ (GRAD)
 // ---------------------------------------------------------------------------
-constexpr int kQB = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kKT = 64;    // keys per tile
+constexpr int kDeltaWaves = 4;   // D pass: 128 queries per workgroup, two workgroups per CU
+constexpr int kGradWaves = 8;    // dQ pass: 256 queries per workgroup, one per CU
 
 enum RowMode { kDelta = 0, kGrad = 1 };
 
@@ -117,20 +122,22 @@ struct QTile {
   static constexpr int kKSteps = D / 16;
   static constexpr int kDBlocks = D / 32;
   static constexpr int kBlocks = (kKT / 4) * (D / 8);
-  static_assert(kBlocks <= kThreads, "one block per thread at most");
+  static_assert(kBlocks <= kThreads, "one block per loader thread (threads 0..255) at most");
 };
 
-// The D pass fits two workgroups per CU (LDS and at most 256 registers per
-// lane), so two waves share each SIMD and hide each other's latency; the dQ
-// pass needs more registers and runs one wave per SIMD.
-template <int D, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(kThreads, MODE == kDelta ? 2 : 1) void rows_kernel(
+// Two waves share each SIMD and hide each other's latency: the D pass as two
+// 4-wave workgroups per CU (68 KiB of LDS each), the dQ pass (104 KiB with
+// its transposed K tile) as one 8-wave workgroup.  Both bounds cap the
+// registers at 256 per lane.
+template <int D, bool CAUSAL, int MODE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int B, int H, int Hkv, int N, float c, float scale,
     int n_qblocks) {
   using T = QTile<D>;
+  constexpr int kRows = 32 * WAVES;   // queries per workgroup
   // double-buffered: tile kt+1 is stored while tile kt is computed
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * T::kRowStride];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * T::kRowStride];
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(kThreads, MODE == kDelta ? 2 : 1) void rows_kernel(
   const int b = bh / H;
   const int h = bh - b * H;
   const int g = h / (H / Hkv);
-  const int q0 = qb * kQB;
+  const int q0 = qb * kRows;
   const size_t head_q = (size_t)bh * N;
   const size_t head_kv = ((size_t)b * Hkv + g) * N;
 
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(kThreads, MODE == kDelta ? 2 : 1) void rows_kernel(
 #pragma unroll
   for (int cb = 0; cb < T::kDBlocks; ++cb) dq[cb] = f32x16_t{};
 
-  const int q_hi = min(q0 + kQB, N);
+  const int q_hi = min(q0 + kRows, N);
   int n_kt = (N + kKT - 1) / kKT;
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kKT + 1);
   const int wq_first = q0 + 32 * wave;
@@ -227,68 +234,56 @@ __global__ __launch_bounds__(kThreads, MODE == kDelta ? 2 : 1) void rows_kernel(
     auto tile_body = [&](auto masked_tag) {
     constexpr bool need_mask = decltype(masked_tag)::value;
 
-    // S^T = K Q^T, dP^T = V dO^T : two 32-key blocks, lane = query, regs = keys
-    f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
-    f32x16_t p_acc[2] = {f32x16_t{}, f32x16_t{}};
+    // The two 32-key halves of the tile, one after the other.
 #pragma unroll
-    for (int s = 0; s < T::kKSteps; ++s) {
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T, dP^T = V dO^T for keys 32*kb .. 32*kb+31: lane = query, regs = keys
+      f32x16_t s_acc = f32x16_t{};
+      f32x16_t p_acc = f32x16_t{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int s = 0; s < T::kKSteps; ++s) {
         const int off = kSwz ? rm_read_off(T::kRowStride, kb, col, s, grp)
                              : (32 * kb + col) * T::kRowStride + 16 * s + 8 * grp;
         const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(&sK[buf][off]);
         const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&sV[buf][off]);
-        s_acc[kb] = mfma_32x32x16_bf16(ak, qf[s], s_acc[kb]);
-        p_acc[kb] = mfma_32x32x16_bf16(av, of[s], p_acc[kb]);
+        s_acc = mfma_32x32x16_bf16(ak, qf[s], s_acc);
+        p_acc = mfma_32x32x16_bf16(av, of[s], p_acc);
       }
-    }
-    sched_reads_ahead<4 * T::kKSteps, 1>();
+      sched_reads_ahead<2 * T::kKSteps, 1, MODE == kDelta ? 4 : 2>();
 
-    float pv[2][16];
+      float pv[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(fmaf(s_acc[kb][r], c, -l2));
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(s_acc[r], c, -l2));
+      if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * grp + (r & 3);
-          if (!qok || (kj >= N) || (CAUSAL && kj > qi)) pv[kb][r] = 0.f;
+          if (!qok || (kj >= N) || (CAUSAL && kj > qi)) pv[r] = 0.f;
         }
-    }
-    u32x4_t ds_hi[2][2], ds_lo[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float ds[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (MODE == kDelta) dsum = fmaf(pv[kb][r], p_acc[kb][r], dsum);
-        else ds[r] = pv[kb][r] * (p_acc[kb][r] - dd);
       }
-      if (MODE == kGrad) {
+      if (MODE == kDelta) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) split_bf16x8(&ds[8 * t], ds_hi[kb][t], ds_lo[kb][t]);
-      }
-    }
-
-    if (MODE == kGrad) {
-      // dQ^T += K^T dS^T
+        for (int r = 0; r < 16; ++r) dsum = fmaf(pv[r], p_acc[r], dsum);
+      } else {
+        float ds[16];
 #pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb) {
+        for (int r = 0; r < 16; ++r) ds[r] = pv[r] * (p_acc[r] - dd);
+        u32x4_t ds_hi[2], ds_lo[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int t = 0; t < 2; ++t) split_bf16x8(&ds[8 * t], ds_hi[t], ds_lo[t]);
+        // dQ^T += K^T dS^T over this half's keys
+#pragma unroll
+        for (int cb = 0; cb < T::kDBlocks; ++cb) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
                 &sKt[buf][tr_read_off(T::kTStride, cb, col, kb, t, grp)]);
-            dq[cb] = mfma_32x32x16_bf16(a, ds_hi[kb][t], dq[cb]);
-            dq[cb] = mfma_32x32x16_bf16(a, ds_lo[kb][t], dq[cb]);
+            dq[cb] = mfma_32x32x16_bf16(a, ds_hi[t], dq[cb]);
+            dq[cb] = mfma_32x32x16_bf16(a, ds_lo[t], dq[cb]);
           }
         }
+        sched_reads_ahead<2 * T::kDBlocks, 2, 2>();
       }
-      sched_reads_ahead<4 * T::kDBlocks, 2>();
     }
     };
     if (wq_first < N && !(CAUSAL && k0 > wq_last)) {
@@ -570,13 +565,14 @@ hipError_t launch_all(const BwdArgs& a) {
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   const uint16_t* dO = static_cast<const uint16_t*>(a.dO);
-  const int n_qb = (a.N + kQB - 1) / kQB;
-  const dim3 row_grid((unsigned)((long long)n_qb * a.B * a.H));
+  const int n_qb_d = (a.N + 32 * kDeltaWaves - 1) / (32 * kDeltaWaves);
+  const int n_qb_g = (a.N + 32 * kGradWaves - 1) / (32 * kGradWaves);
 
-  hipError_t e = launch_kernel(rows_kernel<D, CAUSAL, kDelta>, row_grid, dim3(kThreads), 0,
-                               a.stream, q, k, v, dO, a.lse, a.delta,
+  hipError_t e = launch_kernel(rows_kernel<D, CAUSAL, kDelta, kDeltaWaves>,
+                               dim3((unsigned)((long long)n_qb_d * a.B * a.H)),
+                               dim3(64 * kDeltaWaves), 0, a.stream, q, k, v, dO, a.lse, a.delta,
                                static_cast<uint16_t*>(nullptr), a.B, a.H, a.Hkv, a.N, c, a.scale,
-                               n_qb);
+                               n_qb_d);
   if (e != hipSuccess) return e;
 
   const int n_kb = (a.N + kKB - 1) / kKB;
@@ -586,9 +582,10 @@ hipError_t launch_all(const BwdArgs& a) {
                     a.N, c, a.scale);
   if (e != hipSuccess) return e;
 
-  return launch_kernel(rows_kernel<D, CAUSAL, kGrad>, row_grid, dim3(kThreads), 0, a.stream, q, k,
-                       v, dO, a.lse, a.delta, static_cast<uint16_t*>(a.dq), a.B, a.H, a.Hkv, a.N,
-                       c, a.scale, n_qb);
+  return launch_kernel(rows_kernel<D, CAUSAL, kGrad, kGradWaves>,
+                       dim3((unsigned)((long long)n_qb_g * a.B * a.H)), dim3(64 * kGradWaves), 0,
+                       a.stream, q, k, v, dO, a.lse, a.delta, static_cast<uint16_t*>(a.dq), a.B,
+                       a.H, a.Hkv, a.N, c, a.scale, n_qb_g);
 }
 
 }  // namespace
