@@ -106,6 +106,15 @@ __device__ __forceinline__ int tr_read_off(int stride, int cb, int col, int hb, 
   return (32 * cb + col) * stride + 32 * (hb ^ (cb & 1)) + 16 * (t ^ parity3(col >> 2)) + 8 * grp;
 }
 
+// Copy 16 bytes per lane from global memory at `src` (any address, per lane)
+// into LDS at `lds_wave_dst + 16 * lane` (`lds_wave_dst` must be
+// wave-uniform).  Lanes that are switched off write nothing.  Completion is
+// counted by vmcnt, not seen by the compiler: wait (wait_vmem_all) before a
+// barrier that publishes the data.
+__device__ __forceinline__ void global_load_lds16(const void* src, void* lds_wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_u32_t*)lds_wave_dst, 16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Query-block stationary kernel: D (DELTA) or dQ (GRAD)
 // ---------------------------------------------------------------------------
@@ -192,20 +201,41 @@ __global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kerne
   const int blk_c = kSwz ? 8 * loader_chunk<D>(tid) : 8 * (tid % (D / 8));
   const bool loader = tid < T::kBlocks;
 
-  // Tile kt+1's K and V rows, already in registers, are stored into the other
-  // LDS buffer at the start of iteration kt, then tile kt+2 is loaded into the
-  // registers; both overlap tile kt's compute.  One barrier per tile.
-  u32x4_t kr[4], vr[4];
+  // K: tile kt+1's rows, already in registers, are stored into the other LDS
+  // buffer at the start of iteration kt (row-major, and transposed for dQ),
+  // then tile kt+2 is loaded into the registers.  V: tile kt+1 is copied
+  // global -> LDS by the load unit at the start of iteration kt, straight
+  // into the padded (and, for dQ, swizzled) layout: each 16-byte slot fetches
+  // the chunk that belongs there.  Both overlap tile kt's compute; one barrier
+  // per tile.  Rows past N are zero for K and a copy of row N-1 for V (finite,
+  // and their weights are exactly 0).
+  constexpr int kVSlots = T::kRowStride / 8;           // 16-byte slots per LDS row
+  constexpr int kVCopies = kKT * kVSlots / 64;         // wave-wide copies per tile
+  static_assert((kKT * kVSlots) % 64 == 0, "whole copy instructions");
+  u32x4_t kr[4];
   auto fetch = [&](int k0) {
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kj = k0 + blk_r + r;
-        const bool ok = kj < N;
-        kr[r] = ok ? *reinterpret_cast<const u32x4_t*>(K + (head_kv + kj) * D + blk_c)
-                   : u32x4_t{0, 0, 0, 0};
-        vr[r] = ok ? *reinterpret_cast<const u32x4_t*>(V + (head_kv + kj) * D + blk_c)
-                   : u32x4_t{0, 0, 0, 0};
+        kr[r] = kj < N ? *reinterpret_cast<const u32x4_t*>(K + (head_kv + kj) * D + blk_c)
+                       : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto copy_v = [&](int k0, int buf) {
+#pragma unroll
+    for (int j0 = 0; j0 < kVCopies; j0 += WAVES) {
+      const int j = j0 + wave;
+      if (j < kVCopies) {
+        const int slot_all = 64 * j + lane;
+        const int row = slot_all / kVSlots;
+        const int slot = slot_all - row * kVSlots;
+        if (slot < D / 8) {
+          const int chunk = kSwz ? slot ^ rm_swz(row) : slot;
+          const int kj = min(k0 + row, N - 1);
+          global_load_lds16(V + (head_kv + kj) * D + 8 * chunk, &sV[buf][512 * j]);
+        }
       }
     }
   };
@@ -215,19 +245,23 @@ __global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kerne
       for (int r = 0; r < 4; ++r) {
         const int at = (blk_r + r) * T::kRowStride + (kSwz ? rm_col(blk_r, blk_c) : blk_c);
         *reinterpret_cast<u32x4_t*>(&sK[buf][at]) = kr[r];
-        *reinterpret_cast<u32x4_t*>(&sV[buf][at]) = vr[r];
       }
       if (MODE == kGrad) store_block_transposed_swz(sKt[buf], T::kTStride, blk_c, blk_r, kr);
     }
   };
   fetch(0);
+  copy_v(0, 0);
   stash(0);
   if (n_kt > 1) fetch(kKT);
+  wait_vmem_all();
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int k0 = kt * kKT;
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) stash(buf ^ 1);     // that buffer was last read in iteration kt-1
+    if (kt + 1 < n_kt) {                   // that buffer was last read in iteration kt-1
+      copy_v(k0 + kKT, buf ^ 1);
+      stash(buf ^ 1);
+    }
     if (kt + 2 < n_kt) fetch(k0 + 2 * kKT);
     // Two copies of the tile body, with and without masking, so unmasked tiles
     // carry no per-element compare at all.
@@ -293,6 +327,7 @@ __global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kerne
       else
         tile_body(std::false_type{});
     }
+    wait_vmem_all();   // this wave's V copies of tile kt+1 have landed
     __syncthreads();   // tile kt+1 stored; everyone is done with buffer `buf`
   }
 
