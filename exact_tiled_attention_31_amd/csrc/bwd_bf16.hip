@@ -351,7 +351,7 @@ __global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kerne
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-block stationary
+// dK, dV: key-block stationary (d = 64: two workgroups per CU, two waves per SIMD)
 // ---------------------------------------------------------------------------
 constexpr int kKB = 128;   // keys per workgroup (4 waves x 32)
 constexpr int kQT = 64;    // queries per tile
@@ -367,7 +367,7 @@ struct KVTile {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void dk_dv_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dk_dv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta,
