@@ -16,12 +16,12 @@
 //      dP^T = V dO^T and sums D_i = sum_j P_ij dP_ij in fp32.  D is taken
 //      from the recomputed P and dP rather than from the bf16-rounded O, whose
 //      rounding would otherwise dominate the gradient error.
-//   2. dk_dv: one workgroup per (batch, kv head, 128-key block); each wave
-//      owns 32 keys (lane = key) with its K and V rows in registers and fp32
-//      dK^T, dV^T accumulators; it walks every query head of the group and
-//      every 64-query tile that sees the block: S = Q K^T, P, dP = dO V^T,
-//      dS, dV^T += dO^T P, dK^T += Q^T dS.  Q and dO are staged in LDS
-//      row-major and transposed.
+//   2. dk_dv16: one 8-wave workgroup per (batch, kv head, 128-key block);
+//      each wave owns 16 keys (lane % 16 = key) with their K and V rows in
+//      registers and fp32 dK^T, dV^T accumulators; it walks every query head
+//      of the group and every 64-query tile that sees the block: S = Q K^T, P,
+//      dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.  Q and dO are staged
+//      in LDS row-major and transposed.
 //   3. rows<GRAD>: as 1 with 8-wave workgroups (256 queries), then dS^T and
 //      dQ^T += K^T dS^T.
 // The rows kernels take each 64-key tile as two 32-key halves, one after the
@@ -351,102 +351,124 @@ __global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kerne
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-block stationary (d = 64: two workgroups per CU, two waves per SIMD)
+// dK, dV: key-block stationary.  8 waves x 16 keys = 128 keys per workgroup,
+// with v_mfma_f32_16x16x32_bf16 (16 x 16 fp32 results; lane = 16 * g + c
+// holds column c, rows 4g .. 4g+3).  A 16-key wave's dK^T, dV^T accumulators
+// are half of what a 32-key wave (32 x 32 shape) holds, so the kernel fits
+// 256 registers per lane and two waves share each SIMD; the cost is twice
+// the LDS operand reads per flop.
 // ---------------------------------------------------------------------------
-constexpr int kKB = 128;   // keys per workgroup (4 waves x 32)
+constexpr int kKB = 128;   // keys per workgroup
 constexpr int kQT = 64;    // queries per tile
 
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Position of query q (0..63) in a row of a transposed Q^T / dO^T tile: in
+// each 32-query half, q = 16h + 4g + j goes to 8g + 4h + j, so the queries
+// {4g..4g+3, 16+4g..16+4g+3} that lane group g holds in the 16 x 16 score
+// layout of two 16-query blocks sit at 8 consecutive positions.
+__device__ __forceinline__ int q16_pos(int q) {
+  return (q & ~31) | (q & 3) | (((q >> 4) & 1) << 2) | (((q >> 2) & 3) << 3);
+}
+
+// Bank layout of the staged tiles (gfx950 rules as measured above): loader
+// tl holds query rows 4*(tl & 15) .. +3 and d columns 8*(tl >> 4) .. +7;
+// chunk bit 0 of the row-major tiles and position bit 3 of the transposed
+// tiles are flipped by p(x) = bit 2 ^ bit 3 of the row (query, resp. d).
+// Every operand read and every transposed store is then conflict-free, the
+// row-major stores (the fewest) are 2-way; a CPU model of all four access
+// patterns searched this layout.
+__device__ __forceinline__ int par23(int x) { return ((x >> 2) ^ (x >> 3)) & 1; }
+
 template <int D>
-struct KVTile {
+struct KV16Tile {
   static constexpr int kRowStride = D + 8;     // row-major Q / dO tile (bf16 elements)
   static constexpr int kTStride = kQT + 8;     // transposed Q^T / dO^T tile
-  static constexpr int kKSteps = D / 16;
-  static constexpr int kDBlocks = D / 32;
-  static constexpr int kBlocks = (kQT / 4) * (D / 8);   // 4-row x 8-col blocks per tile
-  static_assert(kBlocks <= kThreads, "one block per thread at most");
+  static constexpr int kKSteps = D / 32;       // 32-wide d steps of S and dP
+  static constexpr int kDBlocks = D / 16;      // 16-row d blocks of dK^T, dV^T
+  static constexpr int kBlocks = (kQT / 4) * (D / 8);   // 4-row x 8-column loader blocks
+  static_assert(kBlocks <= 256, "one block per loader thread");
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dk_dv_kernel(
+__global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int B, int H, int Hkv, int N, float c, float scale) {
-  using T = KVTile<D>;
-  // double-buffered: tile t+1 is stored while tile t is computed
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kQT * T::kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[2][D * T::kTStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[2][kQT * T::kRowStride];   // dO row-major
-  __shared__ __attribute__((aligned(16))) uint16_t sOt[2][D * T::kTStride];      // dO^T
-  __shared__ __attribute__((aligned(16))) float sL[2][kQT];                       // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][kQT];                       // D_i
+  using T = KV16Tile<D>;
+  // [buffer][Q, dO]: row-major tiles and their transposes
+  __shared__ __attribute__((aligned(16))) uint16_t sQO[2][2][kQT * T::kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t sQOt[2][2][D * T::kTStride];
+  __shared__ __attribute__((aligned(16))) float sL[2][kQT];   // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kQT];   // D_i
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;
-  const int grp = lane >> 5;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
 
   const int BG = B * Hkv;
   const int kb = blockIdx.x / BG;     // heavy (early) key blocks first
   const int bg = blockIdx.x - kb * BG;
   const int b = bg / Hkv;
-  const int g = bg - b * Hkv;
+  const int gk = bg - b * Hkv;
   const int k0 = kb * kKB;
-  const int kw0 = k0 + 32 * wave;     // this wave's first key
-  const int key = kw0 + col;          // this lane's key
+  const int kw0 = k0 + 16 * wave;     // this wave's first key
+  const int key = kw0 + c16;          // this lane's key
   const int rep = H / Hkv;
 
-  const size_t head_kv = ((size_t)b * Hkv + g) * N;
-  // K and V rows of this lane's key (B operands over d)
+  const size_t head_kv = ((size_t)b * Hkv + gk) * N;
+  // K and V rows of this lane's key, d = 32 s + 8 g .. +7 (B operands of S, dP)
   u32x4_t kf[T::kKSteps], vf[T::kKSteps];
   {
     const bool ok = key < N;
-    const uint16_t* kr = K + (head_kv + (ok ? key : 0)) * D + 8 * grp;
-    const uint16_t* vr = V + (head_kv + (ok ? key : 0)) * D + 8 * grp;
+    const uint16_t* kr = K + (head_kv + (ok ? key : 0)) * D + 8 * g;
+    const uint16_t* vr = V + (head_kv + (ok ? key : 0)) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < T::kKSteps; ++s) {
-      kf[s] = ok ? *reinterpret_cast<const u32x4_t*>(kr + 16 * s) : u32x4_t{0, 0, 0, 0};
-      vf[s] = ok ? *reinterpret_cast<const u32x4_t*>(vr + 16 * s) : u32x4_t{0, 0, 0, 0};
+      kf[s] = ok ? *reinterpret_cast<const u32x4_t*>(kr + 32 * s) : u32x4_t{0, 0, 0, 0};
+      vf[s] = ok ? *reinterpret_cast<const u32x4_t*>(vr + 32 * s) : u32x4_t{0, 0, 0, 0};
     }
   }
 
-  f32x16_t dk[T::kDBlocks], dv[T::kDBlocks];
+  f32x4_t dk[T::kDBlocks], dv[T::kDBlocks];   // dK^T, dV^T: rows d, column = this lane's key
 #pragma unroll
-  for (int cb = 0; cb < T::kDBlocks; ++cb) {
-    dk[cb] = f32x16_t{};
-    dv[cb] = f32x16_t{};
+  for (int db = 0; db < T::kDBlocks; ++db) {
+    dk[db] = f32x4_t{};
+    dv[db] = f32x4_t{};
   }
 
   const int qt_first = CAUSAL ? (k0 / kQT) : 0;
   const int n_qt = (N + kQT - 1) / kQT;
-  const int blk_r = 4 * loader_kg<D>(tid);    // loader: 4 rows x 8 columns per thread
-  const int blk_c = 8 * loader_chunk<D>(tid);
-  const bool loader = tid < T::kBlocks;
+  // Loaders: waves 0-3 stage Q, waves 4-7 stage dO; loader tl holds rows
+  // blk_r .. blk_r+3 and columns blk_c .. blk_c+7.
+  const int which = tid >> 8;         // 0: Q, 1: dO (wave-uniform)
+  const int tl = tid & 255;
+  const int blk_r = 4 * (tl & 15);
+  const int blk_c = 8 * (tl >> 4);
+  const bool loader = tl < T::kBlocks;
+  const uint16_t* __restrict__ src_rows = which ? dO : Q;
 
-  // Tiles in order: every query tile that sees the block, for each query head
-  // of the group.  Tile t+1's Q, dO rows and statistics, already in registers,
-  // are stored into the other LDS buffer at the start of iteration t, then
-  // tile t+2 is loaded into the registers; both overlap tile t's compute.
-  // One barrier per tile.
   const int tiles_per_head = n_qt - qt_first;
   const int n_tiles = rep * tiles_per_head;
-  u32x4_t qr[4], orow[4];
+  u32x4_t rows[4];
   float lpre = 0.f, dpre = 0.f;
   auto fetch = [&](int t) {
     const int hh = t / tiles_per_head;
     const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
-    const size_t head_q = ((size_t)b * H + g * rep + hh) * N;
+    const size_t head_q = ((size_t)b * H + gk * rep + hh) * N;
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qi = q0 + blk_r + r;
-        const bool ok = qi < N;
-        qr[r] = ok ? *reinterpret_cast<const u32x4_t*>(Q + (head_q + qi) * D + blk_c)
-                   : u32x4_t{0, 0, 0, 0};
-        orow[r] = ok ? *reinterpret_cast<const u32x4_t*>(dO + (head_q + qi) * D + blk_c)
-                     : u32x4_t{0, 0, 0, 0};
+        rows[r] = qi < N ? *reinterpret_cast<const u32x4_t*>(src_rows + (head_q + qi) * D + blk_c)
+                         : u32x4_t{0, 0, 0, 0};
       }
     }
     if (tid < kQT) {
@@ -458,13 +480,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dk_dv_kernel(
   auto stash = [&](int buf) {
     if (loader) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int at = (blk_r + r) * T::kRowStride + rm_col(blk_r, blk_c);
-        *reinterpret_cast<u32x4_t*>(&sQ[buf][at]) = qr[r];
-        *reinterpret_cast<u32x4_t*>(&sO[buf][at]) = orow[r];
+      for (int r = 0; r < 4; ++r)   // rows blk_r .. +3 share bits 2 and 3
+        *reinterpret_cast<u32x4_t*>(
+            &sQO[buf][which][(blk_r + r) * T::kRowStride + (blk_c ^ (8 * par23(blk_r)))]) = rows[r];
+      const int pos0 = q16_pos(blk_r);
+      uint16_t* dst = sQOt[buf][which];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int w = i >> 1;
+        u32x2_t pair;
+        if ((i & 1) == 0) {
+          pair.x = pack_lo_halves(rows[0][w], rows[1][w]);
+          pair.y = pack_lo_halves(rows[2][w], rows[3][w]);
+        } else {
+          pair.x = pack_hi_halves(rows[0][w], rows[1][w]);
+          pair.y = pack_hi_halves(rows[2][w], rows[3][w]);
+        }
+        const int d = blk_c + i;
+        *reinterpret_cast<u32x2_t*>(&dst[d * T::kTStride + (pos0 ^ (8 * par23(d)))]) = pair;
       }
-      store_block_transposed_swz(sQt[buf], T::kTStride, blk_c, blk_r, qr);
-      store_block_transposed_swz(sOt[buf], T::kTStride, blk_c, blk_r, orow);
     }
     if (tid < kQT) {
       sL[buf][tid] = lpre;
@@ -483,89 +517,66 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dk_dv_kernel(
     const int buf = t & 1;
     if (t + 1 < n_tiles) stash(buf ^ 1);   // that buffer was last read in iteration t-1
     if (t + 2 < n_tiles) fetch(t + 2);
-    // this wave's keys kw0..kw0+31 against queries q0..q0+63; skipped when every
-    // query precedes every key
-    // Two copies of the tile body, with and without masking, so unmasked tiles
-    // carry no per-element compare at all.
     auto tile_body = [&](auto masked_tag) {
       constexpr bool need_mask = decltype(masked_tag)::value;
-
-      // S = Q K^T, dP = dO V^T : two 32-query blocks, lane = key, regs = queries
-      f32x16_t s_acc[2] = {f32x16_t{}, f32x16_t{}};
-      f32x16_t p_acc[2] = {f32x16_t{}, f32x16_t{}};
+      // two 32-query halves, one after the other
 #pragma unroll
-      for (int s = 0; s < T::kKSteps; ++s) {
+      for (int h = 0; h < 2; ++h) {
+        // S = Q K^T, dP = dO V^T for query blocks 2h, 2h+1 (16 each): rows =
+        // queries 4g .. 4g+3 of the block, column = this lane's key
+        f32x4_t s_acc[2] = {f32x4_t{}, f32x4_t{}};
+        f32x4_t p_acc[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = rm_read_off(T::kRowStride, qb, col, s, grp);
-          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQ[buf][off]);
-          const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sO[buf][off]);
-          s_acc[qb] = mfma_32x32x16_bf16(aq, kf[s], s_acc[qb]);
-          p_acc[qb] = mfma_32x32x16_bf16(ao, vf[s], p_acc[qb]);
-        }
-      }
-      sched_reads_ahead<4 * T::kKSteps, 1>();
-
-      u32x4_t p_hi[2][2], p_lo[2][2], ds_hi[2][2], ds_lo[2][2];
-      float p[2][16];
+        for (int s = 0; s < T::kKSteps; ++s) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int qq = 32 * qb + 8 * r4 + 4 * grp;    // 4 consecutive query rows
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][qq]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[qb][4 * r4 + e] = fast_exp2(fmaf(s_acc[qb][4 * r4 + e], c, -l4[e]));
-        }
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * grp + (r & 3);
-            if ((qi >= N) || (key >= N) || (CAUSAL && key > qi)) p[qb][r] = 0.f;
-          }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float ds[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t d4 =
-              *reinterpret_cast<const f32x4_t*>(&sD[buf][32 * qb + 8 * r4 + 4 * grp]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            ds[4 * r4 + e] = p[qb][4 * r4 + e] * (p_acc[qb][4 * r4 + e] - d4[e]);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          split_bf16x8(&p[qb][8 * t], p_hi[qb][t], p_lo[qb][t]);
-          split_bf16x8(&ds[8 * t], ds_hi[qb][t], ds_lo[qb][t]);
-        }
-      }
-
-      // dV^T += dO^T P, dK^T += Q^T dS : lane = key, regs = d
-#pragma unroll
-      for (int cb = 0; cb < T::kDBlocks; ++cb) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int off = tr_read_off(T::kTStride, cb, col, qb, t, grp);
-            const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sOt[buf][off]);
-            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQt[buf][off]);
-            dv[cb] = mfma_32x32x16_bf16(ao, p_hi[qb][t], dv[cb]);
-            dv[cb] = mfma_32x32x16_bf16(ao, p_lo[qb][t], dv[cb]);
-            dk[cb] = mfma_32x32x16_bf16(aq, ds_hi[qb][t], dk[cb]);
-            dk[cb] = mfma_32x32x16_bf16(aq, ds_lo[qb][t], dk[cb]);
+          for (int qq = 0; qq < 2; ++qq) {
+            const int off = (16 * (2 * h + qq) + c16) * T::kRowStride + 32 * s + 8 * (g ^ par23(c16));
+            const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQO[buf][0][off]);
+            const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sQO[buf][1][off]);
+            s_acc[qq] = mfma_16x16x32_bf16(aq, kf[s], s_acc[qq]);
+            p_acc[qq] = mfma_16x16x32_bf16(ao, vf[s], p_acc[qq]);
           }
         }
+        sched_reads_ahead<4 * T::kKSteps, 1>();
+
+        // weights and dS for queries 32h + 16 qq + 4g + e (element 4 qq + e)
+        float p[8], ds[8];
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const int ql = 32 * h + 16 * qq + 4 * g;
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][ql]);
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][ql]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float pe = fast_exp2(fmaf(s_acc[qq][e], c, -l4[e]));
+            if (need_mask) {
+              const int qi = q0 + ql + e;
+              if ((qi >= N) || (key >= N) || (CAUSAL && key > qi)) pe = 0.f;
+            }
+            p[4 * qq + e] = pe;
+            ds[4 * qq + e] = pe * (p_acc[qq][e] - d4[e]);
+          }
+        }
+        u32x4_t p_hi, p_lo, ds_hi, ds_lo;
+        split_bf16x8(p, p_hi, p_lo);
+        split_bf16x8(ds, ds_hi, ds_lo);
+
+        // dV^T += dO^T P, dK^T += Q^T dS over this half's 32 queries
+#pragma unroll
+        for (int db = 0; db < T::kDBlocks; ++db) {
+          const int off = (16 * db + c16) * T::kTStride + 32 * h + 8 * (g ^ par23(c16));
+          const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sQOt[buf][1][off]);
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQOt[buf][0][off]);
+          dv[db] = mfma_16x16x32_bf16(ao, p_hi, dv[db]);
+          dv[db] = mfma_16x16x32_bf16(ao, p_lo, dv[db]);
+          dk[db] = mfma_16x16x32_bf16(aq, ds_hi, dk[db]);
+          dk[db] = mfma_16x16x32_bf16(aq, ds_lo, dk[db]);
+        }
+        sched_reads_ahead<2 * T::kDBlocks, 2>();
       }
-      sched_reads_ahead<8 * T::kDBlocks, 2>();
     };
     if (kw0 < N && !(CAUSAL && q0 + kQT - 1 < kw0)) {
-      if ((q0 + kQT > N) || (kw0 + 32 > N) || (CAUSAL && q0 < kw0 + 31))
+      if ((q0 + kQT > N) || (kw0 + 16 > N) || (CAUSAL && q0 < kw0 + 15))
         tile_body(std::true_type{});
       else
         tile_body(std::false_type{});
@@ -577,18 +588,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void dk_dv_kernel(
     uint16_t* dkr = dK + (head_kv + key) * D;
     uint16_t* dvr = dV + (head_kv + key) * D;
 #pragma unroll
-    for (int cb = 0; cb < T::kDBlocks; ++cb) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * cb + 8 * r4 + 4 * grp;
-        u32x2_t wk, wv;
-        wk.x = pack_bf16x2(dk[cb][4 * r4 + 0] * scale, dk[cb][4 * r4 + 1] * scale);
-        wk.y = pack_bf16x2(dk[cb][4 * r4 + 2] * scale, dk[cb][4 * r4 + 3] * scale);
-        wv.x = pack_bf16x2(dv[cb][4 * r4 + 0], dv[cb][4 * r4 + 1]);
-        wv.y = pack_bf16x2(dv[cb][4 * r4 + 2], dv[cb][4 * r4 + 3]);
-        *reinterpret_cast<u32x2_t*>(dkr + d0) = wk;
-        *reinterpret_cast<u32x2_t*>(dvr + d0) = wv;
-      }
+    for (int db = 0; db < T::kDBlocks; ++db) {
+      const int d0 = 16 * db + 4 * g;
+      u32x2_t wk, wv;
+      wk.x = pack_bf16x2(dk[db][0] * scale, dk[db][1] * scale);
+      wk.y = pack_bf16x2(dk[db][2] * scale, dk[db][3] * scale);
+      wv.x = pack_bf16x2(dv[db][0], dv[db][1]);
+      wv.y = pack_bf16x2(dv[db][2], dv[db][3]);
+      *reinterpret_cast<u32x2_t*>(dkr + d0) = wk;
+      *reinterpret_cast<u32x2_t*>(dvr + d0) = wv;
     }
   }
 }
@@ -611,7 +619,7 @@ hipError_t launch_all(const BwdArgs& a) {
   if (e != hipSuccess) return e;
 
   const int n_kb = (a.N + kKB - 1) / kKB;
-  e = launch_kernel(dk_dv_kernel<D, CAUSAL>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(kThreads),
+  e = launch_kernel(dk_dv16_kernel<D, CAUSAL>, dim3((unsigned)(n_kb * a.B * a.Hkv)), dim3(512),
                     0, a.stream, q, k, v, dO, a.lse, static_cast<const float*>(a.delta),
                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.B, a.H, a.Hkv,
                     a.N, c, a.scale);
