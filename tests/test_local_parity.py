@@ -120,3 +120,23 @@ def test_growing_keys_force_many_rebases():
         O, L = oracle.attention_fwd(inp.q, inp.k, inp.v, True, w.scale, window=window)
         check_bf16(dev_bf16_to_f64(o), O, f"local growing w={window}")
         check_lse(dev_to_f64(lse), L, f"local growing w={window}")
+
+
+def test_window_shape_switch():
+    # Windows on both sides of the launch's switch from 4-wave workgroups
+    # (windows up to 2048 keys) to 8-wave workgroups, at a size whose 8-wave
+    # grid fills the chip (32 query heads on 8 kv heads, N=4096): two whole
+    # heads element by element for each window.
+    torch, fa = require_gpu()
+    w = W.small_case("wswitch", "bf16", 1, 32, 8, 4096, 128, True, 215)
+    inp = W.gen_inputs(w)
+    for window in (2048, 2049, 3000):
+        o, lse = run_local(inp, fa, torch, window)
+        for h in (0, w.H - 1):
+            g = oracle.kv_head_of(h, w.H, w.Hkv)
+            O, L = oracle.attention_fwd(inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1],
+                                        True, w.scale, window=window)
+            info = check_bf16(dev_bf16_to_f64(o[:, h:h + 1]), O, f"window {window} head {h}")
+            info["lse_max_abs"] = check_lse(dev_to_f64(lse[:, h:h + 1]), L,
+                                            f"window {window} head {h}")
+            print(f"window {window} head {h}", info, flush=True)
