@@ -50,6 +50,7 @@ constexpr float kNegInf = -__builtin_inff();
 // almost never needed.
 constexpr float kSlack = 48.f;
 constexpr float kSlackSum = 281474976710656.f;   // 2^kSlack
+static_assert(kSlackSum == static_cast<float>(1ull << static_cast<int>(kSlack)), "2^kSlack");
 
 template <int D>
 struct Tile {
@@ -198,8 +199,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
       store_block_transposed(vt, T::kVtStride / 2, 8 * v_dc, 4 * v_kg4, vreg);
     }
   };
-  // copy instructions of one K tile issued by this wave
-  const int my_copies = (T::kKCopies - wave + WAVES - 1) / WAVES;
 
   // ---- running state (log2 units), per 32-row block -------------------------
   float m2[BLOCKS], l[BLOCKS];   // l: this lane's keys only; lane pairs are summed at the end
