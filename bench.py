@@ -16,7 +16,9 @@ JSON line:
             duration comes from HIP events recorded on the launch stream
   cpu_baseline  the float64 oracle on a bounded sample of the same inputs
             (a few query heads, full rows), timed on the host cores.
-Only one GPU is used: --gpus above 1 exits with a message.
+Informational legs (skippable): short sequences, FP8, sliding window, long
+context (N=32768) and the backward.  Only one GPU is used: --gpus above 1
+exits with a message.
 """
 from __future__ import annotations
 
@@ -179,6 +181,35 @@ def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps):
             "steps": steps}
 
 
+def long_context_timing(fa, W, torch, np, dev, stream, warmup, steps):
+    """Informational: the long-context configuration (B=1, 32 query heads on 8
+    kv heads, N=32768, d=128, bf16, causal, seed 4), HIP events on the launch
+    stream, causal-adjusted flops against the dense bf16 peak."""
+    w = W.C4
+    inp = W.gen_inputs(w)
+    q, k, v = (torch.from_numpy(getattr(inp, x + "_bits").view(np.int16)).view(torch.bfloat16)
+               .to(dev) for x in ("q", "k", "v"))
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    tf = w.causal_adjusted_flops() / (ms * 1e-3) / 1e12
+    return {"workload": "long-context causal forward B=1 H=32 Hkv=8 N=32768 d=128 bf16 (seed 4)",
+            "ms": round(ms, 4), "tflops": round(tf, 2),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_convention": "4*B*H*N^2*d/2",
+            "steps": steps}
+
+
 def short_n_sweep(fa, W, torch, np, dev, stream, warmup, steps):
     """Informational: the headline head layout (B=1, 32 query heads on 8 kv
     heads, d=128, bf16, causal) at decode-like short sequence lengths.  These
@@ -226,6 +257,8 @@ def main():
                     help="skip the informational FP8 forward timing")
     ap.add_argument("--no-local", action="store_true",
                     help="skip the informational sliding-window timing (window 256)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the informational long-context timing (N = 32768)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the informational backward timing (B=2 H=16 N=4096 d=128 causal)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -316,6 +349,10 @@ def main():
         out["fp8"] = fp8_timing(fa, W, torch, np, dev, stream, args.warmup, args.steps)
     if not args.no_local:
         out["local"] = local_timing(fa, w, torch, q, k, v, stream, 256, args.warmup, args.steps)
+    if not args.no_long:
+        out["long_context"] = long_context_timing(fa, W, torch, np, dev, stream,
+                                                  max(3, args.warmup // 10),
+                                                  max(3, args.steps // 10))
     if not args.no_backward:
         out["backward"] = backward_timing(fa, W, torch, np, dev, args.warmup, max(5, args.steps // 5))
     if not args.no_cpu_baseline:
