@@ -11,7 +11,7 @@
 //     dV_j = sum_i P_ij dO_i,   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i.
 //
 // Three kernels, no atomics (deterministic):
-//   1. rows<DELTA>: one 4-wave workgroup per (batch, query head, 128-query
+//   1. rows<DELTA>: one 8-wave workgroup per (batch, query head, 256-query
 //      block), lane = query; walks the visible key tiles computing S^T = K Q^T and
 //      dP^T = V dO^T and sums D_i = sum_j P_ij dP_ij in fp32.  D is taken
 //      from the recomputed P and dP rather than from the bf16-rounded O, whose
@@ -22,8 +22,7 @@
 //      of the group and every 64-query tile that sees the block: S = Q K^T, P,
 //      dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.  Q and dO are staged
 //      in LDS row-major and transposed.
-//   3. rows<GRAD>: as 1 with 8-wave workgroups (256 queries), then dS^T and
-//      dQ^T += K^T dS^T.
+//   3. rows<GRAD>: as 1, then dS^T and dQ^T += K^T dS^T.
 // The rows kernels take each 64-key tile as two 32-key halves, one after the
 // other, so only one half's scores, dP and dS are live: both then fit two
 // waves per SIMD (at most 256 registers per lane).
@@ -119,7 +118,7 @@ __device__ __forceinline__ void global_load_lds16(const void* src, void* lds_wav
 // Query-block stationary kernel: D (DELTA) or dQ (GRAD)
 // ---------------------------------------------------------------------------
 constexpr int kKT = 64;    // keys per tile
-constexpr int kDeltaWaves = 4;   // D pass: 128 queries per workgroup, two workgroups per CU
+constexpr int kDeltaWaves = 8;   // D pass: 256 queries per workgroup
 constexpr int kGradWaves = 8;    // dQ pass: 256 queries per workgroup, one per CU
 
 enum RowMode { kDelta = 0, kGrad = 1 };
@@ -134,12 +133,11 @@ struct QTile {
   static_assert(kBlocks <= kThreads, "one block per loader thread (threads 0..255) at most");
 };
 
-// Two waves share each SIMD and hide each other's latency: the D pass as two
-// 4-wave workgroups per CU (68 KiB of LDS each), the dQ pass (104 KiB with
-// its transposed K tile) as one 8-wave workgroup.  Both bounds cap the
-// registers at 256 per lane.
+// Two waves share each SIMD and hide each other's latency: one 8-wave
+// workgroup per CU (68 KiB of LDS for the D pass, 104 KiB for dQ with its
+// transposed K tile).  The bound caps the registers at 256 per lane.
 template <int D, bool CAUSAL, int MODE, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, MODE == kDelta ? 2 : 1) void rows_kernel(
+__global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, float* __restrict__ delta,
