@@ -7,15 +7,22 @@ heads, N=8192, d=128, bf16 storage, causal, scale 1/sqrt(128); Q, K, V iid
 N(0,1) from seed 3 with 1% of key rows per kv head scaled x8.  Inputs are
 generated on the host, copied to HBM once, and are resident before timing.
 
-A step is one fa_fwd call over the whole batch.  W untimed warm-up steps
-(about 0.1 s of work by default, enough for the clock to settle), then K
-steps bracketed by device synchronisation on both sides.  Prints one
-JSON line:
+A step is one fa_fwd call over the whole batch.  First a time-based
+pre-heat (--preheat-s seconds of untimed launches, reported under
+"preheat": the clock needs a few hundred ms of load to reach its sustained
+level), then W untimed warm-up steps, then K steps bracketed by device
+synchronisation on both sides, with a HIP event recorded on the launch
+stream before each step.  Prints one JSON line:
   value     causal-adjusted TFLOP/s = 4*B*H*N^2*d/2 / (wall time per step)
   roofline  the forward kernel against the dense bf16 matrix-core peak; its
-            duration comes from HIP events recorded on the launch stream
+            duration is the median of the per-step event times
+  sclk      graphics clock sampled during the timed steps (SMU metrics), and
+            pct_clock_adjusted_peak = achieved / (peak * sclk / 2400 MHz)
+  flushed   median step time with a 512 MiB buffer written before each step
+            (L2 and Infinity Cache cold)
   cpu_baseline  the float64 oracle on a bounded sample of the same inputs
-            (a few query heads, full rows), timed on the host cores.
+            (all 32 query heads by default, full causal rows; --cpu-heads
+            bounds it), timed on the host cores.
 Informational legs (skippable): short sequences, FP8, sliding window, long
 context (N=32768) and the backward.  Only one GPU is used: --gpus above 1
 exits with a message.
@@ -37,6 +44,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E bandwidth (published)
+PEAK_SCLK_MHZ = 2400.0        # the clock the published peaks assume
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_c3_traffic.json")
 FWD_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_31_amd", "csrc", f)
                for f in ("fwd_bf16.hip", "common.hpp")]
@@ -90,7 +98,151 @@ def cpu_baseline(inp, w, heads: int):
                       f"BLAS threads {blas_threads}"}
 
 
-def backward_timing(fa, W, torch, np, dev, warmup, steps):
+def tile_count_flops(w, rows: int = 32, cols: int = 64) -> float:
+    """The pages' tile-count convention (flops counted per computed tile,
+    4 * rows * cols * d for each (query tile, key tile) pair that is not
+    skipped) for the tile the forward computes: one wave's 32 query rows
+    against a 64-key tile; a key tile is skipped when its first key lies after
+    the wave's last row."""
+    n_q = -(-w.N // rows)
+    tiles = 0
+    for qt in range(n_q):
+        last = min(w.N, (qt + 1) * rows) - 1
+        tiles += (last // cols + 1) if w.causal else -(-w.N // cols)
+    return 4.0 * rows * cols * w.d * tiles * w.B * w.H
+
+
+class ClockSampler:
+    """Samples the graphics clock (MHz, mean over the XCDs reported by the
+    SMU metrics table) in a background thread while a region runs.  Yields
+    None when the management library is unavailable."""
+
+    def __init__(self, period_s: float = 0.002):
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._handle = None
+        self.error = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:   # no library, no permission, no device
+            self.error = f"{type(e).__name__}: {e}"
+            self._handle = None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if xs:
+            return sum(xs) / len(xs)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, (int, float)) and c > 0 else None
+
+    def __enter__(self):
+        import threading
+        if self._handle is None:
+            return self
+        self.samples = []
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    c = self._read()
+                    if c is not None:
+                        self.samples.append(c)
+                except Exception:
+                    pass
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs)}
+
+
+def preheat(torch, call, seconds: float) -> dict:
+    """Untimed load until `seconds` of wall time have passed, so the clock
+    reaches its sustained level before warm-up and timing (the first tens of
+    milliseconds of load run slower)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            call()
+        n += 8
+        torch.cuda.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "launches": n}
+
+
+def timed_steps(torch, call, stream, warmup: int, steps: int):
+    """W untimed steps, then K steps between device synchronisations, with an
+    event recorded on the launch stream before each step and after the last.
+    Returns (wall seconds, per-step event times in ms)."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i].record(stream)
+        call()
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
+def flushed_steps(torch, call, stream, steps: int, flush_bytes: int):
+    """Steps with the L2 and the MALL (Infinity Cache) flushed first: a
+    buffer of `flush_bytes` is written on the launch stream before each step,
+    and only the step itself is timed (events around the call)."""
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device=stream.device)
+    times = []
+    for i in range(steps):
+        buf.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del buf
+    return times
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def event_leg(torch, call, stream, warmup, steps, preheat_s):
+    """Pre-heat, warm-up, then per-step events: (mean ms, median ms)."""
+    if preheat_s > 0:
+        preheat(torch, call, preheat_s)
+    _, ts = timed_steps(torch, call, stream, warmup, steps)
+    return sum(ts) / len(ts), median(ts)
+
+
+def backward_timing(fa, W, torch, np, dev, warmup, steps, preheat_s):
     """Informational: fa_bwd on the backward workload (B=2 H=16 N=4096 d=128
     causal), timed with HIP events on the launch stream.  The rate counts the
     algorithmic work of the gradient, 2.5x the causal-adjusted forward flops
@@ -107,24 +259,19 @@ def backward_timing(fa, W, torch, np, dev, warmup, steps):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(16, fa.fa_bwd_workspace_bytes(w5.B, w5.H, w5.Hkv, w5.N, w5.d)),
                      dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
+
+    def call():
         fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=w5.scale, stream=stream)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(steps):
-        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, scale=w5.scale, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+
+    mean_ms, med_ms = event_leg(torch, call, stream, warmup, steps, preheat_s)
     flops = 2.5 * w5.causal_adjusted_flops()
     return {"workload": "backward B=2 H=16 Hkv=16 N=4096 d=128 bf16 causal (seed 5)",
-            "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "ms": round(med_ms, 4), "ms_mean": round(mean_ms, 4),
+            "tflops": round(flops / (med_ms * 1e-3) / 1e12, 2),
             "flop_convention": "2.5 * 4*B*H*N^2*d/2", "steps": steps}
 
 
-def local_timing(fa, w, torch, q, k, v, stream, window, warmup, steps):
+def local_timing(fa, w, torch, q, k, v, stream, window, warmup, steps, preheat_s):
     """Informational: fa_fwd_local (window 256, the pages' example width) on
     the headline inputs, timed with HIP events on the launch stream.  The rate
     counts 4*d flops per visible (query, key) pair: sum_i min(i+1, window)
@@ -132,23 +279,18 @@ def local_timing(fa, w, torch, q, k, v, stream, window, warmup, steps):
     n = w.N
     pairs = window * (window + 1) // 2 + (n - window) * window if n > window else n * (n + 1) // 2
     flops = 4.0 * w.d * w.B * w.H * pairs
-    for _ in range(warmup):
+
+    def call():
         fa.fa_fwd_local(q, k, v, window, scale=w.scale, stream=stream)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(steps):
-        fa.fa_fwd_local(q, k, v, window, scale=w.scale, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
+
+    mean_ms, med_ms = event_leg(torch, call, stream, warmup, steps, preheat_s)
     return {"workload": f"local causal forward, window {window}, same inputs as the headline",
-            "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "ms": round(med_ms, 5), "ms_mean": round(mean_ms, 5),
+            "tflops": round(flops / (med_ms * 1e-3) / 1e12, 2),
             "flop_convention": "4*d*B*H*sum_i min(i+1, window)", "steps": steps}
 
 
-def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps):
+def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps, preheat_s):
     """Informational: fa_fwd_fp8 on the headline draws quantized to e4m3 with
     per-tensor scales (same shape, causal), HIP events on the launch stream;
     rate against the dense fp8 matrix-core peak."""
@@ -163,25 +305,15 @@ def fp8_timing(fa, W, torch, np, dev, stream, warmup, steps):
         fa.fa_fwd_fp8(q, k, v, ds["q"], ds["k"], ds["v"], o=o, lse=lse, causal=True,
                       scale=w.scale, stream=stream)
 
-    for _ in range(warmup):
-        call()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(steps):
-        call()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
-    tf = w.causal_adjusted_flops() / (ms * 1e-3) / 1e12
+    mean_ms, med_ms = event_leg(torch, call, stream, warmup, steps, preheat_s)
+    tf = w.causal_adjusted_flops() / (med_ms * 1e-3) / 1e12
     return {"workload": "fp8 e4m3 forward, headline shape and draws, per-tensor scales",
-            "ms": round(ms, 5), "tflops": round(tf, 2), "peak_fp8": PEAK_FP8_TFLOPS,
-            "frac": round(tf / PEAK_FP8_TFLOPS, 4), "flop_convention": "4*B*H*N^2*d/2",
-            "steps": steps}
+            "ms": round(med_ms, 5), "ms_mean": round(mean_ms, 5), "tflops": round(tf, 2),
+            "peak_fp8": PEAK_FP8_TFLOPS, "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+            "flop_convention": "4*B*H*N^2*d/2", "steps": steps}
 
 
-def long_context_timing(fa, W, torch, np, dev, stream, warmup, steps):
+def long_context_timing(fa, W, torch, np, dev, stream, warmup, steps, preheat_s):
     """Informational: the long-context configuration (B=1, 32 query heads on 8
     kv heads, N=32768, d=128, bf16, causal, seed 4), HIP events on the launch
     stream, causal-adjusted flops against the dense bf16 peak."""
@@ -192,30 +324,25 @@ def long_context_timing(fa, W, torch, np, dev, stream, warmup, steps):
     del inp
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    for _ in range(warmup):
+
+    def call():
         fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(steps):
-        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / steps
-    tf = w.causal_adjusted_flops() / (ms * 1e-3) / 1e12
+
+    mean_ms, med_ms = event_leg(torch, call, stream, warmup, steps, preheat_s)
+    tf = w.causal_adjusted_flops() / (med_ms * 1e-3) / 1e12
     return {"workload": "long-context causal forward B=1 H=32 Hkv=8 N=32768 d=128 bf16 (seed 4)",
-            "ms": round(ms, 4), "tflops": round(tf, 2),
+            "ms": round(med_ms, 4), "ms_mean": round(mean_ms, 4), "tflops": round(tf, 2),
             "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flop_convention": "4*B*H*N^2*d/2",
             "steps": steps}
 
 
-def short_n_sweep(fa, W, torch, np, dev, stream, warmup, steps):
+def short_n_sweep(fa, W, torch, np, dev, stream, warmup, steps, preheat_s):
     """Informational: the headline head layout (B=1, 32 query heads on 8 kv
     heads, d=128, bf16, causal) at decode-like short sequence lengths.  These
     launches are far too small to be compute-bound; the rate reported is the
     compulsory HBM traffic (Q, K, V read once, O and LSE written once) per
-    kernel duration (HIP events), against the 8 TB/s HBM peak."""
+    kernel duration (median of per-step HIP events), against the 8 TB/s HBM
+    peak."""
     out = []
     for n in (128, 256, 512, 1024):
         w = W.C3.with_(N=n, outlier_frac=0.0)
@@ -224,19 +351,13 @@ def short_n_sweep(fa, W, torch, np, dev, stream, warmup, steps):
                    .to(dev) for x in ("q", "k", "v"))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-        for _ in range(warmup):
+
+        def call():
             fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for _ in range(steps):
-            fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1) / steps
-        gbs = w.compulsory_bytes() / (ms * 1e-3) / 1e9
-        out.append({"N": n, "us": round(ms * 1e3, 2), "compulsory_bytes": w.compulsory_bytes(),
+
+        _, med_ms = event_leg(torch, call, stream, warmup, steps, preheat_s)
+        gbs = w.compulsory_bytes() / (med_ms * 1e-3) / 1e9
+        out.append({"N": n, "us": round(med_ms * 1e3, 2), "compulsory_bytes": w.compulsory_bytes(),
                     "GB_per_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
     return out
 
@@ -245,9 +366,16 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU needs a few hundred ms of load to "
-                         "reach its sustained clock")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before timing")
+    ap.add_argument("--preheat-s", type=float, default=1.0,
+                    help="seconds of untimed load before the warm-up steps (the clock "
+                         "needs a few hundred ms of load to reach its sustained level); "
+                         "reported under 'preheat'")
+    ap.add_argument("--leg-preheat-s", type=float, default=0.3,
+                    help="pre-heat of each informational leg")
+    ap.add_argument("--flush-steps", type=int, default=20,
+                    help="steps timed with the L2 and MALL flushed before each (0: skip)")
+    ap.add_argument("--flush-mib", type=int, default=512, help="flush buffer size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="query heads the oracle baseline computes (bounded sample)")
@@ -299,27 +427,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    def call():
         fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-    torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    clock = ClockSampler()
+    heat = preheat(torch, call, args.preheat_s) if args.preheat_s > 0 else None
+    with clock:
+        wall, step_ms = timed_steps(torch, call, stream, args.warmup, args.steps)
 
     ms_per_step = wall * 1e3 / args.steps
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    kernel_ms_med = median(step_ms)
+    kernel_ms_mean = sum(step_ms) / len(step_ms)
     flops = w.causal_adjusted_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    achieved = flops / (kernel_ms_med * 1e-3) / 1e12
     traffic = measured_traffic()
+    sclk = clock.summary()
 
     out = {
         "metric": "attention fwd TFLOP/s (causal-adjusted) at N=8192 d=128 bf16; % MFMA peak",
@@ -337,24 +460,46 @@ def main():
         "config": {"workload": "GQA causal forward B=1 H=32 Hkv=8 N=8192 d=128 bf16, "
                                "1% of K rows x8 (seed 3)",
                    "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": True,
-                   "flops_per_step": flops, "flop_convention": "4*B*H*N^2*d/2"},
+                   "flops_per_step": flops, "flop_convention": "4*B*H*N^2*d/2",
+                   "flops_tile_count": tile_count_flops(w),
+                   "tile_count_convention": "4*rows*cols*d per computed (32-row, 64-key) "
+                                            "tile; key tiles past a wave's last row skipped"},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": traffic, "kernel_ms": round(kernel_ms_med, 5),
+                     "kernel_ms_mean": round(kernel_ms_mean, 5),
+                     "kernel_ms_stat": "median of per-step HIP events on the launch stream"},
+        "preheat": heat,
+        "sclk": sclk if sclk is not None else {"unavailable": clock.error},
     }
+    if sclk is not None:
+        # the nominal peak assumes 2.4 GHz; the same work at the measured clock
+        adj_peak = PEAK_BF16_TFLOPS * sclk["mean_mhz"] / PEAK_SCLK_MHZ
+        out["pct_clock_adjusted_peak"] = round(100.0 * achieved / adj_peak, 2)
+    if args.flush_steps > 0:
+        fl = flushed_steps(torch, call, stream, args.flush_steps, args.flush_mib * 2 ** 20)
+        fm = median(fl)
+        out["flushed"] = {"ms": round(fm, 5), "tflops": round(flops / (fm * 1e-3) / 1e12, 2),
+                          "frac": round(flops / (fm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "steps": args.flush_steps,
+                          "flush": f"{args.flush_mib} MiB buffer written before each step"}
     if not args.no_short_n:
-        out["short_n"] = short_n_sweep(fa, W, torch, np, dev, stream, args.warmup, args.steps)
+        out["short_n"] = short_n_sweep(fa, W, torch, np, dev, stream, args.warmup, args.steps,
+                                       args.leg_preheat_s)
     if not args.no_fp8:
-        out["fp8"] = fp8_timing(fa, W, torch, np, dev, stream, args.warmup, args.steps)
+        out["fp8"] = fp8_timing(fa, W, torch, np, dev, stream, args.warmup, args.steps,
+                                args.leg_preheat_s)
     if not args.no_local:
-        out["local"] = local_timing(fa, w, torch, q, k, v, stream, 256, args.warmup, args.steps)
+        out["local"] = local_timing(fa, w, torch, q, k, v, stream, 256, args.warmup, args.steps,
+                                    args.leg_preheat_s)
     if not args.no_long:
         out["long_context"] = long_context_timing(fa, W, torch, np, dev, stream,
                                                   max(3, args.warmup // 10),
-                                                  max(3, args.steps // 10))
+                                                  max(3, args.steps // 10), args.leg_preheat_s)
     if not args.no_backward:
-        out["backward"] = backward_timing(fa, W, torch, np, dev, args.warmup, max(5, args.steps // 5))
+        out["backward"] = backward_timing(fa, W, torch, np, dev, args.warmup,
+                                          max(5, args.steps // 5), args.leg_preheat_s)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_heads)
     print(json.dumps(out), flush=True)

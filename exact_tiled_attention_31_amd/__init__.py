@@ -9,7 +9,7 @@ Names mirror the C ABI in ``include/fattn.h``:
     fa_fwd(q, k, v, ...)        bf16 forward  -> (o, lse)
     fa_fwd_f32(q, k, v, ...)    fp32 forward  -> (o, lse)
     fa_fwd_local(q, k, v, window, ...)  bf16 sliding-window causal forward -> (o, lse)
-    fa_fwd_fp8(q, k, v, dq, dk, dv, ...)  FP8 (e4m3) forward -> (o bf16, lse)
+    fa_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, ...)  FP8 (e4m3) forward -> (o bf16, lse)
     fa_bwd(q, k, v, o, lse, dO, ...)  bf16 backward -> (dq, dk, dv)
     fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     fa_status_string(status)

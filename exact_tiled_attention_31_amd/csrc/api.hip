@@ -12,8 +12,12 @@ namespace {
 constexpr long double kMaxElems = 4611686018427387904.0L;   // 2^62
 constexpr long long kMaxRows = 2147483647LL;                // 2^31 - 1
 // The bf16 and fp8 forwards address one head's K and V through a buffer
-// resource with a 32-bit byte range and 32-bit offsets.
+// resource with a 32-bit byte range and signed 32-bit offsets.  The last key
+// tile of a head forms row offsets up to 63 rows past N (those rows read as
+// zero), so N + 64 rows must stay addressable: (N + 64) * d * elem bytes are
+// at most 2^31 - 1.
 constexpr long long kMaxHeadBytes = 2147483647LL;           // 2^31 - 1
+constexpr long long kTileRowSlack = 64;                     // rows past N a key tile may address
 
 struct Range {
   uintptr_t lo, hi;   // [lo, hi)
@@ -48,7 +52,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
   int st = check_sizes(B, H, Hkv, N, d, empty);
   if (st != FA_OK || *empty) return st;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (elem <= 2 && (long long)N * d * (long long)elem > kMaxHeadBytes) return FA_ERR_INVALID_ARG;
+  if (elem <= 2 && ((long long)N + kTileRowSlack) * d * (long long)elem > kMaxHeadBytes)
+    return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4))
@@ -120,7 +125,8 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
 extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
   bool empty = false;
   if (check_sizes(B, H, Hkv, N, d, &empty) != FA_OK || empty) return 0;
-  // D_i = dO_i . O_i per query row, fp32, rounded up to 256 bytes.
+  // D_i = sum_j P_ij dP_ij per query row (recomputed by the backward's D
+  // pass), fp32, rounded up to 256 bytes.
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }

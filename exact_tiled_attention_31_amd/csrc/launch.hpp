@@ -33,7 +33,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: D_i = dO_i . O_i, fp32 [B, H, N]
+  float* delta;  // workspace: D_i = sum_j P_ij dP_ij (recomputed by the D pass), fp32 [B, H, N]
   int B, H, Hkv, N, d;
   bool causal;
   float scale;

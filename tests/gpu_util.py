@@ -91,3 +91,24 @@ def dev_inputs(inp: W.Inputs, torch):
         q, k, v = (f32_to_dev(getattr(inp, n), torch) for n in ("q", "k", "v"))
         do = f32_to_dev(inp.do, torch) if inp.do is not None else None
     return q, k, v, do
+
+
+def fwd_launch_shape(B: int, H: int, Hkv: int, N: int, causal: bool = True, window: int = 0):
+    """(waves per workgroup, query heads per workgroup, workgroups) that the
+    bf16 forward picks for these sizes.  Mirrors the host rule in the
+    forward's launcher: workgroups of 8 waves x 32 rows serve `hp` query heads
+    of one kv head (4, 2 or 1 as the group size allows); the launch falls back
+    to 4-wave workgroups when the 8-wave grid has fewer than 512 workgroups
+    (two per CU) or for a local window of at most 2048 keys."""
+    rep = H // Hkv
+
+    def grid(waves):
+        hp = 4 if rep % 4 == 0 and waves % 4 == 0 else 2 if rep % 2 == 0 and waves % 2 == 0 else 1
+        rows_h = (waves // hp) * 32
+        return hp, -(-N // rows_h) * B * H // hp
+
+    local = causal and 0 < window < N
+    hp8, items8 = grid(8)
+    if (local and window <= 2048) or items8 < 512:
+        return (4, *grid(4))
+    return 8, hp8, items8

@@ -82,9 +82,15 @@ def test_forward_validation(f32):
     for d in (32, 96, 256):
         assert fwd(lib, f32=f32, d=d) == UNS, d
     if not f32:
-        # one head's bf16 K/V slab (N*d*2 bytes) must stay below 2^31
-        for n, d in ((1 << 23, 128), (1 << 24, 64)):
-            assert fwd(lib, H=1, Hkv=1, N=n, d=d) == INV, (n, d)
+        # one head's bf16 K/V slab plus the 64 rows a last key tile may
+        # address, (N + 64) * d * 2 bytes, must stay below 2^31: the first N
+        # past that limit is rejected, including the N just below the plain
+        # N * d * 2 < 2^31 bound, where row offsets of the last tile would
+        # overflow a signed 32-bit offset
+        for d in (128, 64):
+            n_max = (2 ** 31 - 1) // (2 * d) - 64
+            for n in (n_max + 1, (2 ** 31 - 1) // (2 * d), 1 << 24):
+                assert fwd(lib, H=1, Hkv=1, N=n, d=d) == INV, (n, d)
     # empty problems are a no-op and may pass NULL pointers
     for kw in ({"B": 0}, {"N": 0}):
         assert fwd(lib, f32=f32, q=None, k=None, v=None, o=None, lse=None, **kw) == fa.FA_OK
@@ -129,6 +135,9 @@ def test_fp8_validation():
         assert f8(**kw) == INV, kw
     assert f8(d=96) == fa.FA_ERR_UNSUPPORTED
     assert f8(H=1, Hkv=1, N=1 << 24, d=128) == INV        # K slab of 2^31 bytes
+    n_max = (2 ** 31 - 1) // 128 - 64                      # (N + 64) * 128 bytes < 2^31
+    for n in (n_max + 1, (2 ** 31 - 1) // 128):
+        assert f8(H=1, Hkv=1, N=n, d=128) == INV, n
     assert f8(N=0, q=None, dq=0.0) == fa.FA_OK              # empty problem first
 
 

@@ -100,3 +100,20 @@ def test_bwd_rejects_short_workspace():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
         fa.fa_bwd(q, q, q, q, lse, q, workspace=ws, causal=True)
+
+
+def test_bwd_does_not_read_o():
+    # fa_bwd recomputes D_i = sum_j P_ij dP_ij from P and dP instead of
+    # dO_i . O_i, so the `o` argument is validated but never read: an o full
+    # of NaN must leave the gradients bitwise unchanged.
+    torch, fa = require_gpu()
+    inp = W.gen_inputs(W.C5.with_(N=640, B=1, H=4, Hkv=2))
+    w = inp.w
+    q, k, v, do = dev_inputs(inp, torch)
+    o, lse = fa.fa_fwd(q, k, v, causal=True, scale=w.scale)
+    ref = fa.fa_bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    o_nan = torch.full_like(o, float("nan"))
+    got = fa.fa_bwd(q, k, v, o_nan, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, got):
+        assert np.array_equal(dev_bf16_bits(x), dev_bf16_bits(y))
