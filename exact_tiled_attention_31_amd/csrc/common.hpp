@@ -51,7 +51,16 @@ __device__ __forceinline__ u32x4_t pack_bf16x8(const float* x) {
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + lo(w) + hi(w) for a packed bf16 pair w (v_dot2c_f32_bf16 against a
+// pair of ones: the bf16 values are exact in fp32, so this sums exactly the
+// rounded weights that enter a matrix-core step).
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
 
 // Eight fp32 values as a pair of bf16 operands hi + lo, hi = bf16(x) and
 // lo = bf16(x - hi): the sum carries about 16 significant bits, so a product

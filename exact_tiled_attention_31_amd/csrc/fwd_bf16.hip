@@ -201,12 +201,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   };
 
   // ---- running state (log2 units), per 32-row block -------------------------
-  float m2[BLOCKS], l[BLOCKS];   // l: this lane's keys only; lane pairs are summed at the end
+  // l: the fp32 weights (for the LSE); lr: the same weights as rounded to
+  // bf16 for the P.V product, so O is normalised by exactly the weights it
+  // accumulated (without it, a row dominated by one key whose weight rounds
+  // by 2^-9 carries that error into O).  Both cover this lane's keys only;
+  // lane pairs are summed at the end.
+  float m2[BLOCKS], l[BLOCKS], lr[BLOCKS];
   f32x16_t oacc[BLOCKS][T::kDBlocks];
 #pragma unroll
   for (int hf = 0; hf < BLOCKS; ++hf) {
     m2[hf] = kNegInf;
     l[hf] = 0.f;
+    lr[hf] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] = f32x16_t{};
   }
@@ -271,10 +277,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     } else if (first) {
       m2[hf] = row_max();
     }
+    float rsum = 0.f;   // the tile's weights as rounded to bf16
     auto weights = [&]() {
       // a row that has seen no key yet has only -inf scores here: reference 0
       const float m = (LOCAL && m2[hf] == kNegInf) ? 0.f : m2[hf];
-      float sa = 0.f, sb = 0.f;
+      float sa = 0.f, sb = 0.f, ra = 0.f, rb = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float p[16];
@@ -285,7 +292,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
         }
         pf[kb][0] = pack_bf16x8(&p[0]);
         pf[kb][1] = pack_bf16x8(&p[8]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ra = add_bf16_pair(pf[kb][t][0], ra);
+          rb = add_bf16_pair(pf[kb][t][1], rb);
+          ra = add_bf16_pair(pf[kb][t][2], ra);
+          rb = add_bf16_pair(pf[kb][t][3], rb);
+        }
       }
+      rsum = ra + rb;
       return sa + sb;
     };
     float psum = weights();
@@ -295,12 +310,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
       // 1 for a row that has still seen no key (l and O are 0 there)
       const float corr = (m_new == kNegInf) ? 1.f : fast_exp2(m2[hf] - m_new);
       l[hf] *= corr;
+      lr[hf] *= corr;
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] *= corr;
       m2[hf] = m_new;
       psum = weights();
     }
     l[hf] += psum;
+    lr[hf] += rsum;
   };
 
   // V^T operand (32 d x 16 keys) for d-block cb, key block kb, step t: one
@@ -374,12 +391,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     if (kt + 2 < n_kt) issue_k_tile(k0 + 2 * kBN, buf);
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+  // ---- epilogue: O = acc / lr, LSE = (m + log2 l) ln 2 ---------------------
 #pragma unroll
   for (int hf = 0; hf < BLOCKS; ++hf) {
     const float lt = pair_sum(l[hf]);
+    const float lrt = pair_sum(lr[hf]);
     if (qi[hf] < N) {
-      const float inv = 1.f / lt;
+      const float inv = 1.f / lrt;
       uint16_t* orow = O + (head_q + qi[hf]) * D;
 #pragma unroll
       for (int cb = 0; cb < T::kDBlocks; ++cb) {

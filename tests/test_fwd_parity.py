@@ -122,8 +122,9 @@ def test_c3_full_size():
     w = W.C3
     inp = W.gen_inputs(w)
     o, lse = run_fwd(inp, fa, torch)
-    # two whole heads, element by element (first and last query head)
-    for h in (0, w.H - 1):
+    # every head, element by element (rows dominated by one outlier key are
+    # rare; sampling rows alone can miss them)
+    for h in range(w.H):
         g = oracle.kv_head_of(h, w.H, w.Hkv)
         O, L = oracle.attention_fwd(inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1],
                                     True, w.scale)
