@@ -11,6 +11,8 @@ Names mirror the C ABI in ``include/fattn.h``:
     fa_fwd_local(q, k, v, window, ...)  bf16 sliding-window causal forward -> (o, lse)
     fa_fwd_fp8(q, k, v, descale_q, descale_k, descale_v, ...)  FP8 (e4m3) forward -> (o bf16, lse)
     fa_bwd(q, k, v, o, lse, dO, ...)  bf16 backward -> (dq, dk, dv)
+    fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, ...)  the same backward with
+                                the library's fixed device scratch (no workspace)
     fa_bwd_workspace_bytes(B, H, Hkv, N, d)
     fa_status_string(status)
 """
@@ -27,6 +29,7 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
+FA_ERR_TOO_LARGE = -4
 
 # C prototypes (kept in step with include/fattn.h)
 _P = ctypes.c_void_p
@@ -39,6 +42,7 @@ PROTOTYPES = {
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -230,6 +234,33 @@ def fa_bwd(q, k, v, o, lse, do, dq=None, dk=None, dv=None, workspace=None,
     return dq, dk, dv
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = False,
+                   scale: float | None = None, stream=None):
+    """fa_bwd through the allocation-free entry point: the caller passes the
+    output tensors, and the per-row D terms go to the library's fixed device
+    scratch (B*H*N <= 2^22).  Nothing is allocated here or in the library."""
+    torch = _torch()
+    bf = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _need(t, name, bf)
+    B, H, Hkv, N, d = _dims(q, k, v)
+    _need(o, "o", bf, (B, H, N, d))
+    _need(do, "do", bf, (B, H, N, d))
+    _need(lse, "lse", torch.float32, (B, H, N))
+    _need(dq, "dq", bf, (B, H, N, d))
+    _need(dk, "dk", bf, (B, Hkv, N, d))
+    _need(dv, "dv", bf, (B, Hkv, N, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, Hkv, N, d,
+                              int(bool(causal)), float(scale), _stream_of(q, stream))
+    if st != FA_OK:
+        raise FattnError(st, "fa_bwd_noalloc")
+    return dq, dk, dv
+
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
+           "fa_bwd_workspace_bytes", "fa_status_string",
            "FattnError", "lib", "LIB_PATH", "PROTOTYPES",
-           "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"]
+           "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_TOO_LARGE"]

@@ -3,8 +3,19 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fattn.h"
 #include "launch.hpp"
+
+// Fixed device scratch of the allocation-free backward (fa_bwd_noalloc): the
+// per-row D terms, fp32 [B, H, N], for at most kNoAllocRows rows (16 MiB).
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not a device address:
+// its device address is looked up once per device (scratch_on_device) and
+// only that pointer is handed to kernels.
+constexpr long long kNoAllocRows = 1LL << 22;
+static __device__ __align__(256) float scratch[kNoAllocRows];
 
 namespace fattn {
 namespace {
@@ -131,19 +142,24 @@ extern "C" size_t fa_bwd_workspace_bytes(int B, int H, int Hkv, int N, int d) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
-                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                      void* workspace, int B, int H, int Hkv, int N, int d, int causal,
-                      float scale, hipStream_t stream) {
-  bool empty = false;
-  int st = check_sizes(B, H, Hkv, N, d, &empty);
-  if (st != FA_OK || empty) return st;
+namespace fattn {
+namespace {
+
+// Validation shared by fa_bwd and fa_bwd_noalloc; `ws_bytes` is the size of a
+// caller-supplied workspace (checked for alignment and overlap), or 0 when the
+// library's own scratch is used.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, const void* dq, const void* dk, const void* dv,
+              const void* workspace, size_t ws_bytes, int B, int H, int Hkv, int N, int d,
+              float scale, bool* empty) {
+  int st = check_sizes(B, H, Hkv, N, d, empty);
+  if (st != FA_OK || *empty) return st;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
-    return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (ws_bytes && !workspace) return FA_ERR_INVALID_ARG;
   const void* p16[] = {q, k, v, o, dO, dq, dk, dv, workspace};
   for (const void* p : p16)
-    if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+    if (p && !aligned(p, 16)) return FA_ERR_INVALID_ARG;
   if (!aligned(lse, 4)) return FA_ERR_INVALID_ARG;
   const long double qb = (long double)B * H * N * d * 2;
   const long double kvb = (long double)B * Hkv * N * d * 2;
@@ -151,15 +167,77 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const Range in[] = {range_of(q, qb), range_of(k, kvb), range_of(v, kvb),
                       range_of(o, qb), range_of(lse, lb), range_of(dO, qb)};
   const Range out[] = {range_of(dq, qb), range_of(dk, kvb), range_of(dv, kvb),
-                       range_of(workspace, (long double)fa_bwd_workspace_bytes(B, H, Hkv, N, d))};
-  for (int i = 0; i < 4; ++i) {
+                       range_of(workspace, (long double)ws_bytes)};
+  const int n_out = ws_bytes ? 4 : 3;
+  for (int i = 0; i < n_out; ++i) {
     for (const Range& r : in)
       if (overlaps(out[i], r)) return FA_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 4; ++j)
+    for (int j = i + 1; j < n_out; ++j)
       if (overlaps(out[i], out[j])) return FA_ERR_INVALID_ARG;
   }
+  return FA_OK;
+}
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream).  Looked up once per device, with that device
+// current, and kept; later calls reuse it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_device(hipStream_t stream, float** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace fattn
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                      void* workspace, int B, int H, int Hkv, int N, int d, int causal,
+                      float scale, hipStream_t stream) {
+  bool empty = false;
+  const size_t ws_bytes = fa_bwd_workspace_bytes(B, H, Hkv, N, d);
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace, ws_bytes, B, H, Hkv, N, d,
+                     scale, &empty);
+  if (st != FA_OK || empty) return st;
   BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace),
             B, H, Hkv, N, d, causal != 0, scale, stream};
+  return status_of(launch_bwd_bf16(a));
+}
+
+extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                              int B, int H, int Hkv, int N, int d, int causal, float scale,
+                              hipStream_t stream) {
+  bool empty = false;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, nullptr, 0, B, H, Hkv, N, d, scale,
+                     &empty);
+  if (st != FA_OK || empty) return st;
+  if ((long long)B * H * N > kNoAllocRows) return FA_ERR_TOO_LARGE;
+  float* ws = nullptr;
+  if (scratch_on_device(stream, &ws) != hipSuccess) return FA_ERR_HIP;
+  BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, ws, B, H, Hkv, N, d, causal != 0, scale, stream};
   return status_of(launch_bwd_bf16(a));
 }
 
@@ -169,6 +247,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the problem exceeds the fixed scratch of fa_bwd_noalloc";
     default: return "unknown libfattn status";
   }
 }

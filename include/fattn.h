@@ -30,7 +30,8 @@
  * caller.  The library allocates nothing, never synchronises, and enqueues
  * its kernels on `stream` (NULL = the default stream) in order; a call returns
  * as soon as the work is enqueued.  Faults during execution surface at the
- * caller's next synchronisation.  All calls are thread-safe (no global state).
+ * caller's next synchronisation.  All calls are thread-safe; the only global
+ * state is fa_bwd_noalloc's per-GPU scratch (see there).
  *
  * Errors.  Arguments are validated before anything is launched; on a non-zero
  * return nothing was enqueued and no output was touched:
@@ -44,7 +45,9 @@
  *                         (the last key tile addresses up to 64 rows past
  *                         N);
  *     FA_ERR_UNSUPPORTED  a head dimension other than 64 or 128;
- *     FA_ERR_HIP          the HIP runtime refused the launch.
+ *     FA_ERR_HIP          the HIP runtime refused the launch;
+ *     FA_ERR_TOO_LARGE    (fa_bwd_noalloc only) the problem exceeds its fixed
+ *                         scratch.
  * B == 0 or N == 0 is an empty problem: FA_OK, nothing is read, written or
  * launched, and the pointers may be NULL.
  */
@@ -63,7 +66,8 @@ enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1,
     FA_ERR_UNSUPPORTED = -2,
-    FA_ERR_HIP = -3
+    FA_ERR_HIP = -3,
+    FA_ERR_TOO_LARGE = -4
 };
 
 /*
@@ -148,6 +152,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dO, void* dq, void* dk, void* dv, void* workspace,
            int B, int H, int Hkv, int N, int d, int causal, float scale,
            hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same operation, layouts, precision and result as
+ * fa_bwd (bitwise: the same kernels run); the per-row D terms live in a fixed
+ * 16 MiB scratch array that the library holds on each GPU it runs on until
+ * the process ends, so B*H*N may be at most 2^22 (4194304) rows, else
+ * FA_ERR_TOO_LARGE is returned before anything is launched.  No call
+ * allocates or frees memory.  Every call on one GPU shares that GPU's scratch:
+ * calls that overlap in time on one GPU (different streams, or different host
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  The scratch's device address is looked up on the first call on each
+ * device (the device that runs `stream`); a failure there is FA_ERR_HIP.
+ * Errors otherwise as fa_bwd.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int Hkv, int N, int d, int causal, float scale,
+                   hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(int status);

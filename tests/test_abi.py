@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd",
+        ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
          "fa_bwd_workspace_bytes", "fa_status_string"])
 
 
@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     fa, lib = _lib()
-    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP,
+                 fa.FA_ERR_TOO_LARGE):
         s = fa.fa_status_string(code)
         assert s.startswith("FA_")
     assert "unknown" in fa.fa_status_string(12345)
@@ -162,6 +163,32 @@ def test_backward_validation():
         assert bwd(**kw) == INV, kw
     assert bwd(d=80) == fa.FA_ERR_UNSUPPORTED
     assert bwd(N=0, q=None, dq=None) == fa.FA_OK
+
+
+def test_backward_noalloc_validation():
+    # every rejection here returns before the scratch lookup or any launch
+    fa, lib = _lib()
+
+    def nb(**kw):
+        a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], do=P[5], dq=P[6], dk=P[7],
+                 dv=P[8], B=1, H=4, Hkv=2, N=128, d=128, causal=1, scale=0.1)
+        a.update(kw)
+        return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                  a["dk"], a["dv"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                                  a["causal"], a["scale"], None)
+
+    INV = fa.FA_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert nb(**{name: None}) == INV, name
+    for kw in ({"dq": P[0]}, {"dk": P[1]}, {"dv": P[5]}, {"dk": P[8]}, {"H": 5, "Hkv": 2},
+               {"scale": float("nan")}, {"dq": ctypes.c_void_p(A + (6 << 32) + 4)}):
+        assert nb(**kw) == INV, kw
+    assert nb(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert nb(N=0, q=None, dq=None) == fa.FA_OK
+    # the fixed scratch holds 2^22 rows of D: one row more is refused
+    assert nb(B=1, H=1, Hkv=1, N=(1 << 22) + 1) == fa.FA_ERR_TOO_LARGE
+    assert nb(B=2, H=32, Hkv=8, N=65537) == fa.FA_ERR_TOO_LARGE
+    assert "FA_ERR_TOO_LARGE" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
 
 
 def test_binding_rejects_host_tensors():
