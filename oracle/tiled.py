@@ -1,14 +1,14 @@
-"""Tiled attention loop in float64, with the pages' counters (oracle; test
+"""Tiled attention in float64, with the pages' counters (oracle; test
 infrastructure only).
 
-The algorithm follows "LLM Architecture Refresh [3]: Flash Attention Is
-Exact":
-  * section 4 "Tiled attention in 40 lines": an outer loop over query blocks
-    and an inner loop over key/value blocks; per tile, scores = scale * q k^T,
-    the running max and normaliser are updated as in section 2, the
-    accumulator is multiplied by the same correction before the tile's
-    p @ v is added, and the division by the normaliser happens once, after
-    the inner loop;
+The computation follows "LLM Architecture Refresh [3]: Flash Attention Is
+Exact" and "How FlashAttention Uses Tiling":
+  * per query block, each key tile yields its own (max, sum, unnormalised
+    output); partial results over disjoint key sets merge exactly once both
+    are rescaled to a common reference (the update equations of "The Running
+    Statistics", section 2 and 3 of the other page), so folding the tiles in
+    key order is the streaming loop of section 4, with one division at the
+    end;
   * section 7 "Causal masking gets a bonus": a tile whose first key lies
     after the block's last query is skipped and counted, never computed;
   * section 8 "Where the speed actually comes from": per computed tile the
@@ -41,16 +41,53 @@ def _expand_kv(k, H):
     return k[:, idx]
 
 
+def _tile_statistics(s, v_tile):
+    """Statistics of one tile on its own, relative to the tile's own row max
+    ("How FlashAttention Uses Tiling", "Building Intuition: Two Blocks"):
+    (m_t, l_t, u_t) with m_t = max_j s_j, l_t = sum_j exp(s_j - m_t) and the
+    unnormalised output u_t = sum_j exp(s_j - m_t) v_j.  A row whose scores are
+    all -inf (every key masked) gives (-inf, 0, 0)."""
+    m_t = s.max(axis=-1, keepdims=True)
+    shift = np.where(np.isfinite(m_t), m_t, 0.0)
+    w = np.exp(s - shift)
+    return m_t, w.sum(axis=-1, keepdims=True), w @ v_tile
+
+
+def _combine(a, b, rescale_first: bool = True):
+    """Merge two partial results over disjoint key sets ("How FlashAttention
+    Uses Tiling", "The Running Statistics" and "Why the Correction Factor
+    Works"; "LLM Architecture Refresh [3]", section 3): both are brought to the
+    common reference max(m_a, m_b) by the factors exp(m_a - m) and exp(m_b - m)
+    and added.  The merge is associative, so folding tiles in key order gives
+    the streaming result.  ``rescale_first=False`` leaves the first output
+    unscaled (the pages' "quietly wrong" variant; negative control only)."""
+    m_a, l_a, u_a = a
+    m_b, l_b, u_b = b
+    m = np.maximum(m_a, m_b)
+    ref = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(invalid="ignore"):
+        f_a = np.where(np.isfinite(m_a), np.exp(m_a - ref), 0.0)
+        f_b = np.where(np.isfinite(m_b), np.exp(m_b - ref), 0.0)
+    u = (u_a * f_a if rescale_first else u_a) + u_b * f_b
+    return m, l_a * f_a + l_b * f_b, u
+
+
 def tiled_attention(q, k, v, causal: bool, block_q: int, block_k: int,
                     scale: float | None = None, counters: dict | None = None,
                     elem: int = 4, rescale_accumulator: bool = True):
-    """O [B,H,N,d] and LSE [B,H,N] by the tiled loop, float64.
+    """O [B,H,N,d] and LSE [B,H,N] by tiles, float64.
+
+    For each query block, every key tile that is not skipped contributes its
+    own statistics (``_tile_statistics``); they are folded left to right with
+    ``_combine`` and the output is divided by the running sum once, at the end
+    ("LLM Architecture Refresh [3]", section 4; the skip rule of section 7;
+    the counters of section 8).
 
     ``counters`` (if given) accumulates ``blocks_skipped``, ``tiles_computed``,
     ``matmul_flops`` and ``hbm_bytes`` (K/V tile reads, ``elem`` bytes per
     element).  ``rescale_accumulator=False`` plants the pages' "quietly wrong"
-    mistake (the accumulator is not rebased when the max moves); it exists only
-    for the oracle's own sensitivity test.
+    mistake (the output accumulated so far is not rebased when the max moves);
+    it exists only for the oracle's own sensitivity test.
     """
     q = np.asarray(q, dtype=np.float64)
     B, H, N, d = q.shape
@@ -63,43 +100,35 @@ def tiled_attention(q, k, v, causal: bool, block_q: int, block_k: int,
             counters.setdefault(key, 0)
     out = np.empty_like(q)
     lse = np.empty((B, H, N))
-    for i in range(0, N, block_q):
-        qi = q[:, :, i:i + block_q]
-        rows = qi.shape[2]
-        m = np.full((B, H, rows, 1), -np.inf)
-        l = np.zeros((B, H, rows, 1))
-        acc = np.zeros((B, H, rows, d))
-        qpos = np.arange(i, i + rows)
-        for j in range(0, N, block_k):
-            if causal and j > i + rows - 1:
+    for q_start in range(0, N, block_q):
+        q_blk = q[:, :, q_start:q_start + block_q]
+        n_rows = q_blk.shape[2]
+        q_last = q_start + n_rows - 1
+        # the empty partial result: no key seen yet
+        state = (np.full((B, H, n_rows, 1), -np.inf), np.zeros((B, H, n_rows, 1)),
+                 np.zeros((B, H, n_rows, d)))
+        for k_start in range(0, N, block_k):
+            if causal and k_start > q_last:          # wholly in the future
                 if counters is not None:
                     counters["blocks_skipped"] += 1
                 continue
-            kj = k[:, :, j:j + block_k]
-            vj = v[:, :, j:j + block_k]
-            cols = kj.shape[2]
-            s = (qi @ np.swapaxes(kj, -1, -2)) * scale
+            k_blk = k[:, :, k_start:k_start + block_k]
+            n_cols = k_blk.shape[2]
+            s = scale * np.einsum("bhid,bhjd->bhij", q_blk, k_blk)
             if causal:
-                kpos = np.arange(j, j + cols)
-                s = np.where(kpos[None, :] > qpos[:, None], -np.inf, s)
-            m_new = np.maximum(m, s.max(axis=-1, keepdims=True))
-            ref = np.where(np.isfinite(m_new), m_new, 0.0)
-            with np.errstate(invalid="ignore"):
-                corr = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
-            p = np.exp(s - ref)
-            l = l * corr + p.sum(axis=-1, keepdims=True)
-            if rescale_accumulator:
-                acc = acc * corr + p @ vj
-            else:
-                acc = acc + p @ vj
-            m = m_new
+                later = (np.arange(k_start, k_start + n_cols)[None, :]
+                         > np.arange(q_start, q_start + n_rows)[:, None])
+                s = np.where(later, -np.inf, s)
+            tile = _tile_statistics(s, v[:, :, k_start:k_start + n_cols])
+            state = _combine(state, tile, rescale_first=rescale_accumulator)
             if counters is not None:
                 counters["tiles_computed"] += 1
-                counters["matmul_flops"] += 2 * (2 * B * H * rows * cols * d)
-                counters["hbm_bytes"] += 2 * B * H * cols * d * elem
+                counters["matmul_flops"] += 2 * (2 * B * H * n_rows * n_cols * d)
+                counters["hbm_bytes"] += 2 * B * H * n_cols * d * elem
+        m, l, u = state
         with np.errstate(divide="ignore", invalid="ignore"):
-            out[:, :, i:i + rows] = acc / l
-            lse[:, :, i:i + rows] = (m + np.log(l))[..., 0]
+            out[:, :, q_start:q_start + n_rows] = u / l
+            lse[:, :, q_start:q_start + n_rows] = (m + np.log(l))[..., 0]
     return out, lse
 
 
@@ -141,9 +170,7 @@ def sliding_window_attention(q, k, v, window: int, scale: float | None = None):
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     s = (q @ np.swapaxes(k, -1, -2)) * scale
-    pos = np.arange(N)
-    hidden = (pos[None, :] < pos[:, None] - window + 1) | (pos[None, :] > pos[:, None])
-    s = np.where(hidden, -np.inf, s)
-    m = s.max(axis=-1, keepdims=True)
-    e = np.exp(s - m)
-    return (e / e.sum(axis=-1, keepdims=True)) @ v
+    lag = np.arange(N)[:, None] - np.arange(N)[None, :]      # query index - key index
+    s = np.where((lag >= 0) & (lag < window), s, -np.inf)      # the visible band
+    w = np.exp(s - s.max(axis=-1, keepdims=True))
+    return (w / w.sum(axis=-1, keepdims=True)) @ v

@@ -215,3 +215,35 @@ def test_counters_with_ragged_tiles():
         assert cnt["hbm_bytes"] == nqb * 2 * H * n * d * e
         assert cnt["matmul_flops"] == 4 * H * n * n * d
         assert cnt["tiles_computed"] == nqb * -(-n // bk)
+
+
+@pytest.mark.parametrize("order", ["reverse", "tree"])
+def test_partial_results_merge_in_any_order(order):
+    # Partial results over disjoint key tiles combine by rescaling to a common
+    # reference ("How FlashAttention Uses Tiling", "Why the Correction Factor
+    # Works"); the merge is associative and commutative, so folding the tiles
+    # right to left, or as a balanced tree, must give the definition too.  A
+    # merge that scaled the wrong operand or dropped a factor fails here even
+    # when a left fold happens to look right.
+    from oracle.tiled import _combine, _tile_statistics
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, 2, 97, 16))
+    k = rng.standard_normal((1, 2, 97, 16)) * np.linspace(0.5, 4.0, 97)[None, None, :, None]
+    v = rng.standard_normal((1, 2, 97, 16))
+    scale = 0.3
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    tiles = [_tile_statistics(s[..., j:j + 13], v[:, :, j:j + 13]) for j in range(0, 97, 13)]
+    if order == "reverse":
+        state = tiles[-1]
+        for t in reversed(tiles[:-1]):
+            state = _combine(t, state)
+    else:
+        level = tiles
+        while len(level) > 1:
+            level = [(_combine(level[i], level[i + 1]) if i + 1 < len(level) else level[i])
+                     for i in range(0, len(level), 2)]
+        state = level[0]
+    m, l, u = state
+    O, L = attention_fwd(q, k, v, False, scale)
+    assert np.abs(u / l - O).max() < 1e-12
+    assert np.abs((m + np.log(l))[..., 0] - L).max() < 1e-12
