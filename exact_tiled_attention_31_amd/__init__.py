@@ -14,6 +14,7 @@ Names mirror the C ABI in ``include/fattn.h``:
     fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, ...)  the same backward with
                                 the library's fixed device scratch (no workspace)
     fa_bwd_workspace_bytes(B, H, Hkv, N, d)
+    fa_debug_counters(out[4], reset)   (counters_lib(), read_counters(): debug build)
     fa_status_string(status)
 """
 from __future__ import annotations
@@ -24,6 +25,8 @@ import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libfattn.so")
+# the same library built with the forward's device counters (debug build)
+COUNTERS_LIB_PATH = os.path.join(PKG_DIR, "libfattn_counters.so")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -43,6 +46,7 @@ PROTOTYPES = {
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_debug_counters": (_I, [ctypes.POINTER(ctypes.c_ulonglong), _I]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -71,6 +75,30 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
         _lib = h
     return _lib
+
+
+def counters_lib() -> ctypes.CDLL:
+    """The debug build (libfattn_counters.so) with prototypes set: the same C
+    ABI, plus device counters in the bf16 forward that fa_debug_counters
+    reads.  Raises if it is not built."""
+    if not os.path.exists(COUNTERS_LIB_PATH):
+        raise ImportError(f"{COUNTERS_LIB_PATH} is not built; run the build")
+    h = ctypes.CDLL(COUNTERS_LIB_PATH)
+    for name, (res, args) in PROTOTYPES.items():
+        fn = getattr(h, name)
+        fn.restype = res
+        fn.argtypes = args
+    return h
+
+
+def read_counters(handle: ctypes.CDLL, reset: bool = False) -> dict:
+    """fa_debug_counters through `handle` as a dict."""
+    out = (ctypes.c_ulonglong * 4)()
+    st = handle.fa_debug_counters(out, int(bool(reset)))
+    if st != FA_OK:
+        raise FattnError(st, "fa_debug_counters")
+    return dict(zip(("tiles_computed", "tiles_skipped", "tiles_masked", "reference_raises"),
+                    (int(x) for x in out)))
 
 
 def fa_status_string(status: int) -> str:
@@ -261,6 +289,6 @@ def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, causal: bool = False,
 
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
-           "fa_bwd_workspace_bytes", "fa_status_string",
+           "fa_bwd_workspace_bytes", "fa_status_string", "counters_lib", "read_counters",
            "FattnError", "lib", "LIB_PATH", "PROTOTYPES",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_TOO_LARGE"]

@@ -241,6 +241,13 @@ extern "C" int fa_bwd_noalloc(const void* q, const void* k, const void* v, const
   return status_of(launch_bwd_bf16(a));
 }
 
+extern "C" int fa_debug_counters(unsigned long long* out, int reset) {
+  if (!out) return FA_ERR_INVALID_ARG;
+  const hipError_t e = fwd_counters(out, reset != 0);
+  if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";

@@ -42,6 +42,16 @@ namespace fattn {
 namespace {
 
 constexpr int kBN = 64;   // keys per tile
+
+#ifdef FATTN_DEVICE_COUNTERS
+// Debug build only: per-launch totals of the bf16 forward, summed over waves
+// (a tile is one wave's 32 query rows against one 64-key tile):
+//   [0] tiles computed, [1] tiles skipped (key tiles of the sequence a row
+//   block never computes), [2] computed tiles that needed masking,
+//   [3] reference raises (a row block's running max moved after its first
+//   tile, rebasing l and O).
+__device__ unsigned long long g_fwd_counters[4];
+#endif
 constexpr float kNegInf = -__builtin_inff();
 // How far (log2 units) a row max may exceed the running reference before the
 // accumulator is rebased.  Terms stay below 2^48, so sums over N <= 2^31 keys
@@ -217,6 +227,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     for (int cb = 0; cb < T::kDBlocks; ++cb) oacc[hf][cb] = f32x16_t{};
   }
 
+#ifdef FATTN_DEVICE_COUNTERS
+  unsigned n_computed = 0, n_masked = 0, n_raised = 0;
+#endif
+
   // S^T = K Q^T for one block (32 keys x 32 queries per accumulator, two key blocks)
   auto scores = [&](const uint8_t* kt_lds, int hf, f32x16_t (&sacc)[2]) {
     sacc[0] = f32x16_t{};
@@ -305,6 +319,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     };
     float psum = weights();
     if (__builtin_expect(__any(psum > kSlackSum), 0)) {
+#ifdef FATTN_DEVICE_COUNTERS
+      if (!first) ++n_raised;
+#endif
       asm volatile("" ::: "memory");
       const float m_new = fmaxf(m2[hf], row_max());
       // 1 for a row that has still seen no key (l and O are 0 there)
@@ -365,6 +382,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
 #pragma unroll
       for (int hf = 0; hf < BLOCKS; ++hf)
         if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], kt == 0, pf[hf]);
+#ifdef FATTN_DEVICE_COUNTERS
+#pragma unroll
+      for (int hf = 0; hf < BLOCKS; ++hf) {
+        n_computed += act[hf] ? 1 : 0;
+        n_masked += (act[hf] && msk[hf]) ? 1 : 0;
+      }
+#endif
       // O^T += V^T P^T; each V operand is read once and used by every block.
       // The d-block loop is innermost so consecutive matrix-core operations
       // accumulate into different registers (no back-to-back dependency).
@@ -390,6 +414,23 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     __syncthreads();
     if (kt + 2 < n_kt) issue_k_tile(k0 + 2 * kBN, buf);
   }
+
+#ifdef FATTN_DEVICE_COUNTERS
+  {
+    // row blocks that hold rows of the sequence; each could have computed
+    // every key tile of it
+    unsigned blocks = 0;
+#pragma unroll
+    for (int hf = 0; hf < BLOCKS; ++hf) blocks += (wq_first + 32 * hf < N) ? 1 : 0;
+    const unsigned all_tiles = blocks * (unsigned)((N + kBN - 1) / kBN);
+    if (lane == 0) {   // one vector atomic per counter and wave
+      atomicAdd(&g_fwd_counters[0], (unsigned long long)n_computed);
+      atomicAdd(&g_fwd_counters[1], (unsigned long long)(all_tiles - n_computed));
+      atomicAdd(&g_fwd_counters[2], (unsigned long long)n_masked);
+      atomicAdd(&g_fwd_counters[3], (unsigned long long)n_raised);
+    }
+  }
+#endif
 
   // ---- epilogue: O = acc / lr, LSE = (m + log2 l) ln 2 ---------------------
 #pragma unroll
@@ -466,6 +507,21 @@ hipError_t launch_one(const FwdArgs& a) {
 }
 
 }  // namespace
+
+hipError_t fwd_counters(unsigned long long* out, bool reset) {
+#ifdef FATTN_DEVICE_COUNTERS
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_fwd_counters), sizeof(g_fwd_counters));
+  if (e == hipSuccess && reset) {
+    const unsigned long long zero[4] = {0, 0, 0, 0};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_fwd_counters), zero, sizeof(zero));
+  }
+  return e;
+#else
+  (void)out;
+  (void)reset;
+  return hipErrorNotSupported;
+#endif
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
   // a window covering the whole sequence is plain causal attention

@@ -54,6 +54,10 @@ struct Fp8FwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+// Debug builds (FATTN_DEVICE_COUNTERS): copy the bf16 forward's four device
+// counters to `out` (synchronous) and optionally zero them; otherwise
+// hipErrorNotSupported.
+hipError_t fwd_counters(unsigned long long* out, bool reset);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a);
 hipError_t launch_fwd_f32(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);

@@ -173,6 +173,23 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int Hkv, int N, int d, int causal, float scale,
                    hipStream_t stream);
 
+/*
+ * Device counters of the bf16 forward (fa_fwd, fa_fwd_local), for checking
+ * the tile schedule and the rescale rule against a host model: the tile
+ * skipping of "LLM Architecture Refresh [3]: Flash Attention Is Exact",
+ * section 7, and the counters its section 8 keeps.  Only a library built with
+ * the counters (libfattn_counters.so, build option FATTN_DEVICE_COUNTERS)
+ * keeps them; the normal library returns FA_ERR_UNSUPPORTED.  A tile is one
+ * wave's 32 query rows against one 64-key tile.  out[0..3] receive the totals
+ * since the last reset: tiles computed; tiles skipped (key tiles of the
+ * sequence a row block never computes); computed tiles that were masked
+ * (diagonal, window edge or sequence end); reference raises (a row block's
+ * running max moved after its first tile, rebasing l and O).  Synchronises
+ * with the device; reset != 0 zeroes the counters afterwards.  out must hold
+ * 4 values (FA_ERR_INVALID_ARG when NULL).
+ */
+int fa_debug_counters(unsigned long long* out, int reset);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* fa_status_string(int status);
 

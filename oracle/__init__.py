@@ -31,12 +31,12 @@ the pages print, closed forms, invariants or brute force.  No function is
 from .attention import (attention_fwd, attention_rows, attention_bwd,
                         attention_probs, kv_head_of)
 from .online_softmax import online_normaliser, online_softmax, softmax_direct
-from .tiled import (tiled_attention, causal_tile_counts, naive_counts,
+from .tiled import (tiled_attention, causal_tile_counts, tile_counts, naive_counts,
                     sliding_window_attention)
 
 __all__ = [
     "attention_fwd", "attention_rows", "attention_bwd", "attention_probs",
     "kv_head_of", "online_normaliser", "online_softmax", "softmax_direct",
-    "tiled_attention", "causal_tile_counts", "naive_counts",
+    "tiled_attention", "causal_tile_counts", "tile_counts", "naive_counts",
     "sliding_window_attention",
 ]

@@ -146,6 +146,26 @@ def causal_tile_counts(n: int, block: int):
     return computed, skipped
 
 
+def tile_counts(n: int, block_q: int, block_k: int, causal: bool = True):
+    """(computed, skipped, masked) tiles of the loop over query blocks of
+    ``block_q`` rows and key blocks of ``block_k`` keys on a square n x n
+    problem.  A tile is skipped when its first key lies after the query
+    block's last row ("LLM Architecture Refresh [3]", section 7); a computed
+    tile is masked when it holds a key after the block's first row (section 5)
+    or the sequence ends inside it.  Counted by walking the grid."""
+    computed = skipped = masked = 0
+    for i in range(0, n, block_q):
+        last = min(i + block_q, n) - 1
+        for j in range(0, n, block_k):
+            if causal and j > last:
+                skipped += 1
+                continue
+            computed += 1
+            if (causal and j + block_k - 1 > i) or j + block_k > n:
+                masked += 1
+    return computed, skipped, masked
+
+
 def naive_counts(batch: int, heads: int, n: int, d: int, elem: int = 4):
     """Counts for standard attention (section 1 and section 8 of the same page):
     two full n x n matmuls; the score matrix crosses HBM four times (write S,

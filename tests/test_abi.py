@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_documented_calls():
     assert declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_f32", "fa_fwd_local", "fa_fwd_fp8", "fa_bwd", "fa_bwd_noalloc",
-         "fa_bwd_workspace_bytes", "fa_status_string"])
+         "fa_bwd_workspace_bytes", "fa_debug_counters", "fa_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -189,6 +189,20 @@ def test_backward_noalloc_validation():
     assert nb(B=1, H=1, Hkv=1, N=(1 << 22) + 1) == fa.FA_ERR_TOO_LARGE
     assert nb(B=2, H=32, Hkv=8, N=65537) == fa.FA_ERR_TOO_LARGE
     assert "FA_ERR_TOO_LARGE" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
+
+
+def test_debug_counters_only_in_the_counters_build():
+    # the normal library keeps no counters; both builds export the call and
+    # reject a NULL output before touching the device
+    fa, lib = _lib()
+    out = (ctypes.c_ulonglong * 4)()
+    assert lib.fa_debug_counters(out, 0) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_debug_counters(None, 0) == fa.FA_ERR_INVALID_ARG
+    if os.path.exists(fa.COUNTERS_LIB_PATH):
+        dbg = fa.counters_lib()
+        assert dbg.fa_debug_counters(None, 1) == fa.FA_ERR_INVALID_ARG
+        for name in declared_functions():
+            assert hasattr(dbg, name), name
 
 
 def test_binding_rejects_host_tensors():

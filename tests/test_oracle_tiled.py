@@ -247,3 +247,30 @@ def test_partial_results_merge_in_any_order(order):
     O, L = attention_fwd(q, k, v, False, scale)
     assert np.abs(u / l - O).max() < 1e-12
     assert np.abs((m + np.log(l))[..., 0] - L).max() < 1e-12
+
+
+def test_rectangular_tile_counts():
+    # Square blocks reduce to the pages' causal table; rectangular blocks agree
+    # with the emulator's own counters (skip rule of section 7) and with the
+    # closed form of a 32-row x 64-key grid (query block t computes
+    # floor(t/2) + 1 key tiles); masked tiles are the computed tiles that hold
+    # a key after the block's first row: one per query block when block_k is
+    # a multiple of block_q.
+    from oracle import tile_counts
+    for n, b in ((2048, 128), (2048, 256), (2048, 512), (300, 64)):
+        c, s, _ = tile_counts(n, b, b, True)
+        assert (c, s) == causal_tile_counts(n, b)
+    n = 8192
+    c, s, m = tile_counts(n, 32, 64, True)
+    assert c == sum(t // 2 + 1 for t in range(n // 32)) == 16512
+    assert c + s == (n // 32) * (n // 64)
+    assert m == n // 32
+    for n, bq, bk, causal in ((300, 32, 64, True), (257, 64, 32, True), (200, 32, 64, False)):
+        ctr = {}
+        q = np.zeros((1, 1, n, 2))
+        tiled_attention(q, q, q, causal, bq, bk, scale=1.0, counters=ctr)
+        c, s, m = tile_counts(n, bq, bk, causal)
+        assert (c, s) == (ctr["tiles_computed"], ctr["blocks_skipped"]), (n, bq, bk)
+    # non-causal: every tile computed; only the ragged last key tile is masked
+    assert tile_counts(200, 32, 64, False) == (7 * 4, 0, 7)
+    assert tile_counts(256, 32, 64, False) == (8 * 4, 0, 0)
