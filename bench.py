@@ -120,6 +120,7 @@ class ClockSampler:
     def __init__(self, period_s: float = 0.002):
         self.period = period_s
         self.samples = []
+        self.avg_samples = []
         self._stop = None
         self._thread = None
         self._handle = None
@@ -135,26 +136,33 @@ class ClockSampler:
             self._handle = None
 
     def _read(self):
+        """(current clock averaged over the XCDs, the SMU's own average
+        clock) in MHz; either may be None."""
         m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
         xs = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        if xs:
-            return sum(xs) / len(xs)
-        c = m.get("current_gfxclk")
-        return float(c) if isinstance(c, (int, float)) and c > 0 else None
+        cur = sum(xs) / len(xs) if xs else None
+        if cur is None:
+            c = m.get("current_gfxclk")
+            cur = float(c) if isinstance(c, (int, float)) and c > 0 else None
+        a = m.get("average_gfxclk_frequency")
+        return cur, (float(a) if isinstance(a, (int, float)) and a > 0 else None)
 
     def __enter__(self):
         import threading
         if self._handle is None:
             return self
         self.samples = []
+        self.avg_samples = []
         self._stop = threading.Event()
 
         def loop():
             while not self._stop.is_set():
                 try:
-                    c = self._read()
-                    if c is not None:
-                        self.samples.append(c)
+                    cur, avg = self._read()
+                    if cur is not None:
+                        self.samples.append(cur)
+                    if avg is not None:
+                        self.avg_samples.append(avg)
                 except Exception:
                     pass
                 self._stop.wait(self.period)
@@ -173,8 +181,14 @@ class ClockSampler:
         if not self.samples:
             return None
         xs = sorted(self.samples)
-        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
-                "samples": len(xs)}
+        out = {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
+               "samples": len(xs),
+               "source": "SMU metrics table (amdsmi), current_gfxclks averaged over the "
+                         "XCDs; updated by firmware, so short regions give few distinct "
+                         "readings"}
+        if self.avg_samples:
+            out["smu_average_mhz"] = round(sum(self.avg_samples) / len(self.avg_samples), 1)
+        return out
 
 
 def preheat(torch, call, seconds: float) -> dict:
@@ -431,7 +445,11 @@ def main():
         fa.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=w.scale, stream=stream)
 
     clock = ClockSampler()
-    heat = preheat(torch, call, args.preheat_s) if args.preheat_s > 0 else None
+    heat = None
+    if args.preheat_s > 0:
+        with clock:
+            heat = preheat(torch, call, args.preheat_s)
+        heat["sclk"] = clock.summary()
     with clock:
         wall, step_ms = timed_steps(torch, call, stream, args.warmup, args.steps)
 
