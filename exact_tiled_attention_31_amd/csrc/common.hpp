@@ -24,9 +24,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -194,45 +192,8 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, void* lds_wave_d
   fattn_llvm_raw_buffer_load_lds(rsrc, (lds_u32_t*)lds_wave_dst, 16, voffset, 0, 0, 0);
 }
 
-// Wait until this wave's outstanding vector-memory operations (including
-// buffer -> LDS copies) number at most N.
-template <int N>
-__device__ __forceinline__ void wait_vmem_at_most() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// Wait until this wave's vector-memory operations (including buffer -> LDS
+// copies) have completed.
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Wait until at most n (wave-uniform, 0..15) vector-memory operations are
-// outstanding.
-__device__ __forceinline__ void wait_vmem_leq(int n) {
-  switch (n) {
-    case 0: wait_vmem_at_most<0>(); break;
-    case 1: wait_vmem_at_most<1>(); break;
-    case 2: wait_vmem_at_most<2>(); break;
-    case 3: wait_vmem_at_most<3>(); break;
-    case 4: wait_vmem_at_most<4>(); break;
-    case 5: wait_vmem_at_most<5>(); break;
-    case 6: wait_vmem_at_most<6>(); break;
-    case 7: wait_vmem_at_most<7>(); break;
-    case 8: wait_vmem_at_most<8>(); break;
-    case 9: wait_vmem_at_most<9>(); break;
-    case 10: wait_vmem_at_most<10>(); break;
-    case 11: wait_vmem_at_most<11>(); break;
-    case 12: wait_vmem_at_most<12>(); break;
-    case 13: wait_vmem_at_most<13>(); break;
-    case 14: wait_vmem_at_most<14>(); break;
-    default: wait_vmem_at_most<15>(); break;
-  }
-}
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane 4j+q supplies the
-// address of 4 consecutive 16-bit elements; lane g receives element g%4 of
-// the chunks supplied by lanes g/4, 4 + g/4, 8 + g/4, 12 + g/4 (in that order).
-// With lane 4j+q pointing at row r0+j, columns c0+4q.., lane g gets column
-// c0+g of rows r0..r0+3.
-__device__ __forceinline__ u32x2_t ds_read_tr16_b64(const void* lds_addr) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds_addr);
-  return __builtin_bit_cast(u32x2_t, v);
-}
 
 }  // namespace fattn
