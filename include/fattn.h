@@ -115,8 +115,11 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                float descale_q, float descale_k, float descale_v, hipStream_t stream);
 
 /*
- * Forward, fp32 storage and fp32 arithmetic throughout (the variant for
- * single-precision inputs; same operation, layout and errors as fa_fwd).
+ * Forward, fp32 storage and fp32 arithmetic throughout: the same exact
+ * attention as fa_fwd ("LLM Architecture Refresh [3]: Flash Attention Is
+ * Exact", section 4, the tiled loop; "How FlashAttention Uses Tiling",
+ * "The Running Statistics"), for single-precision inputs.  Same layout,
+ * ownership and errors as fa_fwd.
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int Hkv, int N, int d, int causal, float scale,
