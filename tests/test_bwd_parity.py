@@ -52,6 +52,16 @@ SMALL = [
     ("d128_N17", 1, 2, 2, 17, 128, True, 206),
     ("d128_N129", 1, 2, 2, 129, 128, False, 207),
     ("d128_gqa8_N700", 1, 8, 1, 700, 128, True, 208),
+    # every (d, causal, group size) combination of the dK/dV instances: P and dS
+    # enter as one bf16 value for one head per kv head, P as a hi + lo pair
+    # from two heads on, dS as well from four on
+    ("d128_noncausal_gqa2", 1, 4, 2, 200, 128, False, 209),
+    ("d128_noncausal_gqa4", 1, 4, 1, 200, 128, False, 210),
+    ("d128_causal_gqa3", 1, 6, 2, 400, 128, True, 214),
+    ("d64_causal_mha", 1, 2, 2, 330, 64, True, 211),
+    ("d64_causal_gqa3", 1, 6, 2, 260, 64, True, 212),
+    ("d64_noncausal_gqa2", 1, 4, 2, 200, 64, False, 215),
+    ("d64_noncausal_gqa8", 1, 8, 1, 200, 64, False, 213),
 ]
 
 
