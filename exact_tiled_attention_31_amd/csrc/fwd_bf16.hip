@@ -13,11 +13,12 @@
 // never leave registers.
 //
 // Mapping onto CDNA4:
-//   * a workgroup of W waves owns W*R query rows (R = 32 or 64 rows per wave,
-//     held as R/32 blocks of 32); each wave keeps its Q fragments, fp32 output
-//     accumulators (AGPRs) and m, l in registers.  With R = 32 two waves share
-//     each SIMD, so one wave's softmax and LDS waits overlap the other's
-//     matrix-core work;
+//   * a workgroup of W waves owns W*32 query rows; each wave keeps its Q
+//     fragments, fp32 output accumulators and m, l in VGPRs (at most 256 per
+//     lane, so two waves share each SIMD and one wave's softmax and LDS waits
+//     can overlap the other's matrix-core work).  The BLOCKS parameter also
+//     builds 64-row waves (two 32-row blocks, one wave per SIMD), a shape that
+//     measured slower and is not launched;
 //   * 64-key tiles of K are copied global -> LDS by the buffer unit
 //     (buffer_load_dwordx4 ... lds, 16 bytes per lane, no VGPR staging) into
 //     rows padded by 16 bytes (the copy points pad slots past the end of the
@@ -28,8 +29,8 @@
 //     query row and the score accumulator becomes the P^T operand of
 //     O^T += V^T P^T without leaving registers.  Every K and V^T operand is a
 //     single conflict-free ds_read_b128 at a base register plus an immediate
-//     (a transpose read would need two instructions per operand, and LDS
-//     instruction issue, not bytes, is what bounds this loop);
+//     (a transpose read would need two instructions per operand, which
+//     measured slower);
 //   * the running reference is raised lazily (see softmax_block), so the
 //     common path has no cross-lane reduction and never touches O;
 //   * exponentials are base 2 with scale*log2(e) folded into one FMA; the
