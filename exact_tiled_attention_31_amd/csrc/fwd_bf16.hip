@@ -100,21 +100,31 @@ __device__ __forceinline__ void interleave_reads_and_mfma() {
 
 // LOCAL (which implies CAUSAL): query i sees keys i - window + 1 .. i only;
 // key tiles older than every row of the workgroup are never loaded.
-template <int D, bool CAUSAL, bool LOCAL, int WAVES, int BLOCKS>
+// SPLIT > 1 (short sequences): the waves form SPLIT groups that take turns
+// over the key tiles (group sp takes tiles sp, sp + SPLIT, ...), each with its
+// own running statistics; the groups' partial results over disjoint key sets
+// are merged at the end by the rebase identity.  The serial chain of key
+// tiles per workgroup is SPLIT times shorter.
+template <int D, bool CAUSAL, bool LOCAL, int WAVES, int BLOCKS, int SPLIT = 1>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int B, int H, int Hkv, int N, float c, int neg_q, int n_qblocks, int window, int hp) {
   static_assert(CAUSAL || !LOCAL, "local attention is causal");
+  static_assert(SPLIT == 1 || (!LOCAL && BLOCKS == 1), "key split: plain attention, 32-row waves");
   using T = Tile<D>;
   constexpr int kRowsPerWave = 32 * BLOCKS;
   // [buffer][K tile | V tile]
   constexpr int kStage = T::kKTile + T::kVTile;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SPLIT * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  constexpr int kSplitWaves = WAVES / SPLIT;            // waves per key-split group
+  const int sp = SPLIT > 1 ? wave / kSplitWaves : 0;    // this wave's group
+  const int wl = SPLIT > 1 ? wave - sp * kSplitWaves : wave;   // wave within the group
+  const int tid_l = SPLIT > 1 ? tid - 64 * kSplitWaves * sp : tid;
   const int col = lane & 31;
   const int grp = lane >> 5;
 
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   // rows_h query rows in each; heavy causal query blocks first.  All waves of
   // the workgroup then see the same causal extent, and one K/V tile serves
   // every head of the group.
-  const int wph = WAVES / hp;                    // waves per query head
+  const int wph = kSplitWaves / hp;              // waves per query head
   const int rows_h = wph * kRowsPerWave;         // query rows per head
   const int rep = H / Hkv;
   const int n_groups = B * Hkv * (rep / hp);
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   const int hs = grp_id - bg * (rep / hp);
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
-  const int h = g * rep + hs * hp + wave / wph;  // this wave's query head
+  const int h = g * rep + hs * hp + wl / wph;    // this wave's query head
   const int q0 = qb * rows_h;
 
   const size_t head_q = ((size_t)b * H + h) * N;
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   const i32x4_t k_rsrc = make_buffer_rsrc(K + head_kv * D, (uint32_t)N * T::kRowBytes);
   const i32x4_t v_rsrc = make_buffer_rsrc(V + head_kv * D, (uint32_t)N * T::kRowBytes);
 
-  const int wq_first = q0 + (wave % wph) * kRowsPerWave;   // this wave's first query row
+  const int wq_first = q0 + (wl % wph) * kRowsPerWave;   // this wave's first query row
   int qi[BLOCKS];
 #pragma unroll
   for (int hf = 0; hf < BLOCKS; ++hf) qi[hf] = wq_first + 32 * hf + col;
@@ -182,8 +192,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     uint8_t* kdst = smem + buf * kStage;
     const int base = k0 * T::kRowBytes;
 #pragma unroll
-    for (int j0 = 0; j0 < T::kKCopies; j0 += WAVES) {
-      const int j = j0 + wave;
+    for (int j0 = 0; j0 < T::kKCopies; j0 += kSplitWaves) {
+      const int j = j0 + wl;
       if (j < T::kKCopies) {
         const int off = copy_offset(64 * j + lane, T::kKSlots);
         buffer_load_lds16(k_rsrc, kdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
@@ -193,9 +203,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
   // V goes through registers so it can be stored transposed: thread = (4-key
   // group, 8-column chunk), key group fastest, so the 8-byte transposed stores
   // of one wave cover whole V^T rows without bank conflicts.
-  const int v_kg4 = tid & 15;
-  const int v_dc = tid >> 4;
-  const bool v_loader = tid < T::kVBlocks;
+  const int v_kg4 = tid_l & 15;
+  const int v_dc = tid_l >> 4;
+  const bool v_loader = tid_l < T::kVBlocks;
   u32x4_t vreg[4];
   auto load_v_tile = [&](int k0) {
     if (v_loader) {
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
       return pair_max(smax) * c;
     };
-    if (LOCAL) {
+    if (LOCAL || SPLIT > 1) {
       // a row's first visible key may lie in any tile: take the row max on
       // the first tile that shows the row a key (m2 stays -inf until then)
       if (__any(m2[hf] == kNegInf)) {
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     float rsum = 0.f;   // the tile's weights as rounded to bf16
     auto weights = [&]() {
       // a row that has seen no key yet has only -inf scores here: reference 0
-      const float m = (LOCAL && m2[hf] == kNegInf) ? 0.f : m2[hf];
+      const float m = ((LOCAL || SPLIT > 1) && m2[hf] == kNegInf) ? 0.f : m2[hf];
       float sa = 0.f, sb = 0.f, ra = 0.f, rb = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -347,27 +357,32 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
                                              2 * (32 * kb + 16 * t));
   };
 
-  // ---- main loop: one barrier per tile, LDS double-buffered ----------------
-  load_v_tile(kt_begin * kBN);
-  issue_k_tile(kt_begin * kBN, 0);
+  // ---- main loop: one barrier per step, LDS double-buffered; a step covers
+  // SPLIT consecutive tiles, of which group sp takes the sp-th --------------
+  const int t0 = kt_begin + sp;   // this group's first tile
+  if (SPLIT == 1 || t0 < n_kt) {
+    load_v_tile(t0 * kBN);
+    issue_k_tile(t0 * kBN, sp);
+  }
   wait_vmem_all();
-  store_v_tile(0);
-  if (kt_begin + 1 < n_kt) issue_k_tile((kt_begin + 1) * kBN, 1);
+  if (SPLIT == 1 || t0 < n_kt) store_v_tile(sp);
+  if (t0 + SPLIT < n_kt) issue_k_tile((t0 + SPLIT) * kBN, SPLIT + sp);
   __syncthreads();
 
-  for (int kt = kt_begin; kt < n_kt; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    const int k0 = kt * kBN;
-    const uint8_t* kt_lds = smem + buf * kStage;
+  for (int kt = kt_begin; kt < n_kt; kt += SPLIT) {
+    const int my = kt + sp;   // this group's tile in this step
+    const int buf = ((kt - kt_begin) / SPLIT) & 1;
+    const int k0 = my * kBN;
+    const uint8_t* kt_lds = smem + (buf * SPLIT + sp) * kStage;
     const uint8_t* vt_lds = kt_lds + T::kKTile;
-    if (kt + 1 < n_kt) load_v_tile(k0 + kBN);   // lands during this tile's compute
+    if (my + SPLIT < n_kt) load_v_tile(k0 + SPLIT * kBN);   // lands during this step
 
     bool act[BLOCKS], msk[BLOCKS];
     bool any_act = false;
 #pragma unroll
     for (int hf = 0; hf < BLOCKS; ++hf) {
       const int first = wq_first + 32 * hf;
-      act[hf] = (first < N) && !(CAUSAL && k0 > first + 31) &&
+      act[hf] = (SPLIT == 1 || my < n_kt) && (first < N) && !(CAUSAL && k0 > first + 31) &&
                 !(LOCAL && first - (k0 + kBN - 1) >= window);
       msk[hf] = (k0 + kBN > N) || (CAUSAL && k0 + kBN - 1 > first) ||
                 (LOCAL && first + 31 - k0 >= window);
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
         if (act[hf]) scores(kt_lds, hf, sacc[hf]);
 #pragma unroll
       for (int hf = 0; hf < BLOCKS; ++hf)
-        if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], kt == 0, pf[hf]);
+        if (act[hf]) softmax_block(sacc[hf], hf, k0, msk[hf], my == 0, pf[hf]);
 #ifdef FATTN_DEVICE_COUNTERS
 #pragma unroll
       for (int hf = 0; hf < BLOCKS; ++hf) {
@@ -411,9 +426,48 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     // other buffer, which nobody has read since the previous barrier; then every
     // wave must be done with buffer `buf` before its K is overwritten
     wait_vmem_all();
-    if (kt + 1 < n_kt) store_v_tile(buf ^ 1);
+    if (my + SPLIT < n_kt) store_v_tile((buf ^ 1) * SPLIT + sp);
     __syncthreads();
-    if (kt + 2 < n_kt) issue_k_tile(k0 + 2 * kBN, buf);
+    if (my + 2 * SPLIT < n_kt) issue_k_tile(k0 + 2 * SPLIT * kBN, buf * SPLIT + sp);
+  }
+
+  if constexpr (SPLIT > 1) {
+    // Groups sp > 0 hand their (m, l, lr, O) to group 0 through LDS (every
+    // tile read ended before the loop's last barrier); group 0 brings both
+    // partial results to their common reference and adds them ("How
+    // FlashAttention Uses Tiling", "Why the Correction Factor Works").
+    constexpr int kVals = 3 + 16 * T::kDBlocks;
+    float* xch = reinterpret_cast<float*>(smem);
+    static_assert((SPLIT - 1) * kSplitWaves * kVals * 64 * 4 <= 2 * SPLIT * kStage, "exchange");
+    if (sp > 0) {
+      float* mine = xch + ((sp - 1) * kSplitWaves + wl) * kVals * 64 + lane;
+      mine[0] = m2[0];
+      mine[64] = l[0];
+      mine[128] = lr[0];
+#pragma unroll
+      for (int cb = 0; cb < T::kDBlocks; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(3 + 16 * cb + r) * 64] = oacc[0][cb][r];
+    }
+    __syncthreads();
+    if (sp == 0) {
+#pragma unroll
+      for (int o = 1; o < SPLIT; ++o) {
+        const float* th = xch + ((o - 1) * kSplitWaves + wl) * kVals * 64 + lane;
+        const float m1 = th[0];
+        const float mm = fmaxf(m2[0], m1);
+        const float f0 = m2[0] == kNegInf ? 0.f : fast_exp2(m2[0] - mm);
+        const float f1 = m1 == kNegInf ? 0.f : fast_exp2(m1 - mm);
+        l[0] = l[0] * f0 + th[64] * f1;
+        lr[0] = lr[0] * f0 + th[128] * f1;
+#pragma unroll
+        for (int cb = 0; cb < T::kDBlocks; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            oacc[0][cb][r] = oacc[0][cb][r] * f0 + th[(3 + 16 * cb + r) * 64] * f1;
+        m2[0] = mm;
+      }
+    }
   }
 
 #ifdef FATTN_DEVICE_COUNTERS
@@ -423,10 +477,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     unsigned blocks = 0;
 #pragma unroll
     for (int hf = 0; hf < BLOCKS; ++hf) blocks += (wq_first + 32 * hf < N) ? 1 : 0;
-    const unsigned all_tiles = blocks * (unsigned)((N + kBN - 1) / kBN);
+    // (with a key split, group 0 accounts for the whole row block: the
+    // additions below are modulo 2^64, so the sum over the groups is exact)
+    const unsigned long long all_tiles =
+        sp == 0 ? (unsigned long long)blocks * (unsigned long long)((N + kBN - 1) / kBN) : 0ull;
     if (lane == 0) {   // one vector atomic per counter and wave
       atomicAdd(&g_fwd_counters[0], (unsigned long long)n_computed);
-      atomicAdd(&g_fwd_counters[1], (unsigned long long)(all_tiles - n_computed));
+      atomicAdd(&g_fwd_counters[1], all_tiles - (unsigned long long)n_computed);
       atomicAdd(&g_fwd_counters[2], (unsigned long long)n_masked);
       atomicAdd(&g_fwd_counters[3], (unsigned long long)n_raised);
     }
@@ -434,6 +491,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
 #endif
 
   // ---- epilogue: O = acc / lr, LSE = (m + log2 l) ln 2 ---------------------
+  if (SPLIT > 1 && sp != 0) return;
 #pragma unroll
   for (int hf = 0; hf < BLOCKS; ++hf) {
     const float lt = pair_sum(l[hf]);
@@ -458,9 +516,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
 }
 
 // Workgroup shape: 8 waves (two per SIMD) of one 32-row block each.  Short
-// sequences, whose 8-wave grid would leave CUs idle, use 4-wave workgroups
-// (two per CU) instead: twice the workgroups, half the rows on each one's
-// serial chain of key tiles.
+// sequences, whose 8-wave grid would leave CUs idle, use the 4-wave shape's
+// grid (twice the workgroups, half the rows on each one's serial chain of key
+// tiles): as 4-wave workgroups (two per CU), or, for causal rows of at least
+// kSplitMinN keys, as 8-wave workgroups whose two wave groups take alternate
+// key tiles and merge their partial results.
 constexpr int kBlocks = 1;
 
 template <int WAVES>
@@ -491,7 +551,23 @@ hipError_t launch_shape(const FwdArgs& a) {
                        a.B, a.H, a.Hkv, a.N, c, neg_q, n_qblocks, a.window, hp);
 }
 
+// Short sequences: 8-wave workgroups over the 4-wave shape's grid, the waves
+// in two groups that take alternate key tiles (half the serial chain).
+template <int D, bool CAUSAL>
+hipError_t launch_split(const FwdArgs& a) {
+  int hp = 1, n_qblocks = 0;
+  const long long items = grid_items<4>(a, &hp, &n_qblocks);
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+  const int neg_q = a.scale < 0.f ? 1 : 0;
+  return launch_kernel(fwd_bf16_kernel<D, CAUSAL, false, 8, kBlocks, 2>, dim3((unsigned)items),
+                       dim3(512), 0, a.stream, static_cast<const uint16_t*>(a.q),
+                       static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                       static_cast<uint16_t*>(a.o), a.lse, a.B, a.H, a.Hkv, a.N, c, neg_q,
+                       n_qblocks, a.window, hp);
+}
+
 constexpr long long kSmallGrid = 2 * 256;   // 8-wave workgroups: fewer than two per CU
+constexpr int kSplitMinN = 512;
 // Local attention with a window up to this many keys gives each workgroup a
 // short chain of key tiles; two 4-wave workgroups per CU then overlap one's
 // start-up with the other's tiles (measured on the 8192-row GQA shape: 11%
@@ -502,8 +578,15 @@ constexpr int kLocalShortWindow = 2048;
 template <int D, bool CAUSAL, bool LOCAL>
 hipError_t launch_one(const FwdArgs& a) {
   int hp = 1, n_qblocks = 0;
-  if ((LOCAL && a.window <= kLocalShortWindow) || grid_items<8>(a, &hp, &n_qblocks) < kSmallGrid)
+  if (LOCAL && a.window <= kLocalShortWindow) return launch_shape<D, CAUSAL, LOCAL, 4>(a);
+  if (grid_items<8>(a, &hp, &n_qblocks) < kSmallGrid) {
+    // the key split pays where the causal chain is long enough (measured on
+    // B=1 H=32 Hkv=8 d=128: N=512 -4%, 1024 -14%, 2048 -10%; N=128/256 and
+    // non-causal rows, whose tiles all carry the same work, did not gain)
+    if constexpr (CAUSAL && !LOCAL)
+      if (a.N >= kSplitMinN) return launch_split<D, CAUSAL>(a);
     return launch_shape<D, CAUSAL, LOCAL, 4>(a);
+  }
   return launch_shape<D, CAUSAL, LOCAL, 8>(a);
 }
 

@@ -4,7 +4,8 @@ heads, N=8192, d=128, causal, 1% of key rows x8).
 
   * tiles computed / skipped / masked against the oracle's walk of the tile
     grid (32-row x 64-key tiles; "LLM Architecture Refresh [3]: Flash
-    Attention Is Exact", section 7, and the counters of section 8);
+    Attention Is Exact", section 7, and the counters of section 8), also on
+    the key-split path of short causal sequences;
   * reference raises against a host replay of the kernel's documented rule:
     a row block takes its reference from the row max of key tile 0; on each
     later tile, if any lane's sum of exp2(s*c - m) over its 32 keys exceeds
@@ -115,3 +116,31 @@ def test_counters_noncausal_ragged_and_reset():
     assert got["tiles_skipped"] == 0 and skipped == 0
     assert got["tiles_masked"] == 2 * heads * masked
     assert fa.read_counters(dbg)["tiles_computed"] == 0
+
+
+def test_counters_on_the_key_split_path():
+    # causal rows of 600 keys on a small grid: two wave groups take alternate
+    # key tiles of each row block; every (row block, tile) pair is still
+    # computed once, and group 0 accounts for the block's skipped tiles
+    torch, fa = require_gpu()
+    dbg = fa.counters_lib()
+    w = W.small_case("ctr_split", "bf16", 2, 4, 2, 600, 128, True, 602)
+    inp = W.gen_inputs(w)
+    q, k, v, _ = dev_inputs(inp, torch)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+    fa.read_counters(dbg, reset=True)
+    assert dbg.fa_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                      ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                      ctypes.c_void_p(lse.data_ptr()), w.B, w.H, w.Hkv, w.N, w.d, 1,
+                      w.scale, None) == fa.FA_OK
+    torch.cuda.synchronize()
+    got = fa.read_counters(dbg, reset=True)
+    computed, skipped, masked = oracle.tile_counts(w.N, ROWS, KEYS, True)
+    heads = w.B * w.H
+    assert got["tiles_computed"] == heads * computed
+    assert got["tiles_skipped"] == heads * skipped
+    assert got["tiles_masked"] == heads * masked
+    o2, l2 = fa.fa_fwd(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)

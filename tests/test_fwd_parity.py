@@ -48,6 +48,10 @@ SMALL = [
     ("bf16_d128_N128", "bf16", 1, 2, 2, 128, 128, True, 109),
     ("bf16_d128_N129", "bf16", 1, 2, 2, 129, 128, False, 110),
     ("bf16_d128_N1000_gqa8", "bf16", 1, 8, 1, 1000, 128, True, 111),
+    # causal rows of 512+ keys on small grids take the key-split path; these
+    # two put one and two query heads in a workgroup
+    ("bf16_d128_N600_gqa2_split", "bf16", 2, 4, 2, 600, 128, True, 112),
+    ("bf16_d64_N700_mha_split", "bf16", 1, 2, 2, 700, 64, True, 113),
     ("f32_d64_causal_ragged", "f32", 2, 4, 2, 300, 64, True, 121),
     ("f32_d128_noncausal_ragged", "f32", 1, 4, 4, 200, 128, False, 122),
     ("f32_d128_causal", "f32", 1, 2, 1, 256, 128, True, 123),
