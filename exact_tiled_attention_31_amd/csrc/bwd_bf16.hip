@@ -199,20 +199,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
   const int blk_c = kSwz ? 8 * loader_chunk<D>(tid) : 8 * (tid % (D / 8));
   const bool loader = tid < T::kBlocks;
 
-  // K: tile kt+1's rows, already in registers, are stored into the other LDS
-  // buffer at the start of iteration kt (row-major, and transposed for dQ),
-  // then tile kt+2 is loaded into the registers.  V: tile kt+1 is copied
-  // global -> LDS by the load unit at the start of iteration kt, straight
-  // into the padded (and, for dQ, swizzled) layout: each 16-byte slot fetches
-  // the chunk that belongs there.  Both overlap tile kt's compute; one barrier
-  // per tile.  Rows past N are zero for K and a copy of row N-1 for V (finite,
-  // and their weights are exactly 0).
+  // dQ pass, K: tile kt+1's rows, already in registers, are stored into the
+  // other LDS buffer at the start of iteration kt (row-major and transposed),
+  // then tile kt+2 is loaded into the registers.  V (and K in the D pass, which
+  // needs no transposed K): tile kt+1 is copied global -> LDS by the load unit
+  // at the start of iteration kt, straight into the padded (and, for dQ,
+  // swizzled) layout: each 16-byte slot fetches the chunk that belongs there.
+  // Both overlap tile kt's compute; one barrier per tile.  Rows past N are
+  // zero for K in registers and a copy of row N-1 when copied (finite, and
+  // their weights are exactly 0).
   constexpr int kVSlots = T::kRowStride / 8;           // 16-byte slots per LDS row
   constexpr int kVCopies = kKT * kVSlots / 64;         // wave-wide copies per tile
   static_assert((kKT * kVSlots) % 64 == 0, "whole copy instructions");
   u32x4_t kr[4];
   auto fetch = [&](int k0) {
-    if (loader) {
+    if (MODE == kGrad && loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kj = k0 + blk_r + r;
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
       }
     }
   };
-  auto copy_v = [&](int k0, int buf) {
+  auto copy_rows = [&](const uint16_t* __restrict__ src, uint16_t* dst, int k0) {
 #pragma unroll
     for (int j0 = 0; j0 < kVCopies; j0 += WAVES) {
       const int j = j0 + wave;
@@ -232,13 +233,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
         if (slot < D / 8) {
           const int chunk = kSwz ? slot ^ rm_swz(row) : slot;
           const int kj = min(k0 + row, N - 1);
-          global_load_lds16(V + (head_kv + kj) * D + 8 * chunk, &sV[buf][512 * j]);
+          global_load_lds16(src + (head_kv + kj) * D + 8 * chunk, dst + 512 * j);
         }
       }
     }
   };
+  // the D pass has no transposed K tile: K is copied by the load unit as V is
+  auto copy_v = [&](int k0, int buf) {
+    copy_rows(V, sV[buf], k0);
+    if constexpr (MODE == kDelta) copy_rows(K, sK[buf], k0);
+  };
   auto stash = [&](int buf) {
-    if (loader) {
+    if (MODE == kGrad && loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int at = (blk_r + r) * T::kRowStride + (kSwz ? rm_col(blk_r, blk_c) : blk_c);
