@@ -22,11 +22,11 @@ namespace {
 
 constexpr long double kMaxElems = 4611686018427387904.0L;   // 2^62
 constexpr long long kMaxRows = 2147483647LL;                // 2^31 - 1
-// The bf16 and fp8 forwards address one head's K and V through a buffer
-// resource with a 32-bit byte range and signed 32-bit offsets.  The last key
-// tile of a head forms row offsets up to 63 rows past N (those rows read as
-// zero), so N + 64 rows must stay addressable: (N + 64) * d * elem bytes are
-// at most 2^31 - 1.
+// The bf16 and fp8 forwards address one head's K and V, and the backward's
+// dK/dV kernel one head's Q and dO, through a buffer resource with a 32-bit
+// byte range and signed 32-bit offsets.  The last tile of a head forms row
+// offsets up to 63 rows past N (those rows read as zero), so N + 64 rows must
+// stay addressable: (N + 64) * d * elem bytes are at most 2^31 - 1.
 constexpr long long kMaxHeadBytes = 2147483647LL;           // 2^31 - 1
 constexpr long long kTileRowSlack = 64;                     // rows past N a key tile may address
 
@@ -155,6 +155,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
   int st = check_sizes(B, H, Hkv, N, d, empty);
   if (st != FA_OK || *empty) return st;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (((long long)N + kTileRowSlack) * d * 2 > kMaxHeadBytes) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (ws_bytes && !workspace) return FA_ERR_INVALID_ARG;
   const void* p16[] = {q, k, v, o, dO, dq, dk, dv, workspace};

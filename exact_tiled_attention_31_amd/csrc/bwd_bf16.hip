@@ -397,6 +397,22 @@ struct KV16Tile {
   static_assert(kBlocks <= 256, "one block per loader thread");
 };
 
+// Interleave `mfmas` matrix-core steps (and their `reads` LDS operand reads,
+// four issued ahead) with the VALU work of another half of the tile: each
+// matrix-core step is followed by up to `valu` VALU instructions.
+template <int reads, int mfmas, int valu>
+__device__ __forceinline__ void sched_mix() {
+  constexpr int kValu = 0x002, kMfma = 0x008, kDsRead = 0x100;
+  constexpr int lead = reads < 4 ? reads : 4;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, lead, 0);
+#pragma unroll
+  for (int i = 0; i < mfmas; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, valu, 0);
+    if (i * reads / mfmas + lead < reads) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+}
+
 // SPLIT_P, SPLIT_DS: P enters dV, resp. dS enters dK, as a hi + lo bf16
 // pair (see the launch for when); otherwise as one bf16 value.
 template <int D, bool CAUSAL, bool SPLIT_P, bool SPLIT_DS>
@@ -454,7 +470,7 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
   const int n_qt = (N + kQT - 1) / kQT;
   // Loaders: waves 0-3 stage Q, waves 4-7 stage dO; loader tl holds rows
   // blk_r .. blk_r+3 and columns blk_c .. blk_c+7.
-  const int which = tid >> 8;         // 0: Q, 1: dO (wave-uniform)
+  const int which = __builtin_amdgcn_readfirstlane(tid >> 8);   // 0: Q, 1: dO (wave-uniform)
   const int tl = tid & 255;
   const int blk_r = 4 * (tl & 15);
   const int blk_c = 8 * (tl >> 4);
@@ -463,19 +479,25 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
 
   const int tiles_per_head = n_qt - qt_first;
   const int n_tiles = rep * tiles_per_head;
-  u32x4_t rows[4];
-  float lpre = 0.f, dpre = 0.f;
-  auto fetch = [&](int t) {
+  // Tiles are fetched three ahead into two register sets (tile j into set
+  // j & 1), which hides the load latency behind two tiles of compute.
+  u32x4_t rows2[2][4];
+  float lpre2[2] = {0.f, 0.f}, dpre2[2] = {0.f, 0.f};
+  auto fetch = [&](int t, auto set_tag) {
+    constexpr int set = decltype(set_tag)::value;
+    u32x4_t* rows = rows2[set];
+    float& lpre = lpre2[set];
+    float& dpre = dpre2[set];
     const int hh = t / tiles_per_head;
     const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
     const size_t head_q = ((size_t)b * H + gk * rep + hh) * N;
     if (loader) {
+      // one head's rows through a range-checked buffer: rows past N read as
+      // zero, and the byte offsets stay below 2^31 (checked at the API)
+      const i32x4_t rs = make_buffer_rsrc(src_rows + head_q * D, (uint32_t)N * D * 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qi = q0 + blk_r + r;
-        rows[r] = qi < N ? *reinterpret_cast<const u32x4_t*>(src_rows + (head_q + qi) * D + blk_c)
-                         : u32x4_t{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r)
+        rows[r] = buffer_load_b128(rs, ((q0 + blk_r + r) * D + blk_c) * 2);
     }
     if (tid < kQT) {
       const int qi = q0 + tid;
@@ -483,7 +505,11 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
       dpre = qi < N ? delta[head_q + qi] : 0.f;
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, auto set_tag) {
+    constexpr int set = decltype(set_tag)::value;
+    const u32x4_t* rows = rows2[set];
+    const float lpre = lpre2[set];
+    const float dpre = dpre2[set];
     if (loader) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)   // rows blk_r .. +3 share bits 2 and 3
@@ -511,27 +537,35 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
       sD[buf][tid] = dpre;
     }
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   if (n_tiles > 0) {
-    fetch(0);
-    stash(0);
-    if (n_tiles > 1) fetch(1);
+    fetch(0, S0{});
+    stash(0, S0{});
+    if (n_tiles > 1) fetch(1, S1{});
+    if (n_tiles > 2) fetch(2, S0{});
   }
   __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
+  // iteration t; set_tag names the register set holding tile t+1
+  auto iter = [&](int t, auto set_tag) {
     const int hh = t / tiles_per_head;
     const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
     const int buf = t & 1;
-    if (t + 1 < n_tiles) stash(buf ^ 1);   // that buffer was last read in iteration t-1
-    if (t + 2 < n_tiles) fetch(t + 2);
+    if (t + 1 < n_tiles) stash(buf ^ 1, set_tag);   // that buffer was last read in iteration t-1
+    if (t + 3 < n_tiles) fetch(t + 3, set_tag);     // the set stash just emptied
     auto tile_body = [&](auto masked_tag) {
       constexpr bool need_mask = decltype(masked_tag)::value;
-      // two 32-query halves, one after the other
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // S = Q K^T, dP = dO V^T for query blocks 2h, 2h+1 (16 each): rows =
-        // queries 4g .. 4g+3 of the block, column = this lane's key
-        f32x4_t s_acc[2] = {f32x4_t{}, f32x4_t{}};
-        f32x4_t p_acc[2] = {f32x4_t{}, f32x4_t{}};
+      // Two 32-query halves, software-pipelined inside the wave: the S, dP
+      // products of half 1 run while half 0's weights are formed, and half
+      // 0's dK, dV products while half 1's are (the arithmetic of each half
+      // is unchanged).
+      f32x4_t s_acc[2][2], p_acc[2][2];   // [half][16-query block]
+      f32x4_t lq[2][2], dq4[2][2];        // LSE * log2(e) and D of the lane's queries
+      u32x4_t p_hi[2], p_lo[2], ds_hi[2], ds_lo[2];
+      // S = Q K^T, dP = dO V^T for query blocks 2h, 2h+1 (16 each): rows =
+      // queries 4g .. 4g+3 of the block, column = this lane's key
+      auto sp_products = [&](int h) __attribute__((always_inline)) {
+        s_acc[h][0] = s_acc[h][1] = p_acc[h][0] = p_acc[h][1] = f32x4_t{};
 #pragma unroll
         for (int s = 0; s < T::kKSteps; ++s) {
 #pragma unroll
@@ -539,49 +573,69 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
             const int off = (16 * (2 * h + qq) + c16) * T::kRowStride + 32 * s + 8 * (g ^ par23(c16));
             const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQO[buf][0][off]);
             const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sQO[buf][1][off]);
-            s_acc[qq] = mfma_16x16x32_bf16(aq, kf[s], s_acc[qq]);
-            p_acc[qq] = mfma_16x16x32_bf16(ao, vf[s], p_acc[qq]);
+            s_acc[h][qq] = mfma_16x16x32_bf16(aq, kf[s], s_acc[h][qq]);
+            p_acc[h][qq] = mfma_16x16x32_bf16(ao, vf[s], p_acc[h][qq]);
           }
         }
-        sched_reads_ahead<4 * T::kKSteps, 1>();
-
-        // weights and dS for queries 32h + 16 qq + 4g + e (element 4 qq + e)
+      };
+      // weights and dS for queries 32h + 16 qq + 4g + e (element 4 qq + e)
+      auto weights = [&](int h) __attribute__((always_inline)) {
         float p[8], ds[8];
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
           const int ql = 32 * h + 16 * qq + 4 * g;
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&sL[buf][ql]);
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&sD[buf][ql]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float pe = fast_exp2(fmaf(s_acc[qq][e], c, -l4[e]));
+            float pe = fast_exp2(fmaf(s_acc[h][qq][e], c, -lq[h][qq][e]));
             if (need_mask) {
               const int qi = q0 + ql + e;
               if ((qi >= N) || (key >= N) || (CAUSAL && key > qi)) pe = 0.f;
             }
             p[4 * qq + e] = pe;
-            ds[4 * qq + e] = pe * (p_acc[qq][e] - d4[e]);
+            ds[4 * qq + e] = pe * (p_acc[h][qq][e] - dq4[h][qq][e]);
           }
         }
-        u32x4_t p_hi, p_lo, ds_hi, ds_lo;
-        if constexpr (SPLIT_P) split_bf16x8(p, p_hi, p_lo);
-        else p_hi = pack_bf16x8(p);
-        if constexpr (SPLIT_DS) split_bf16x8(ds, ds_hi, ds_lo);
-        else ds_hi = pack_bf16x8(ds);
-
-        // dV^T += dO^T P, dK^T += Q^T dS over this half's 32 queries
+        if constexpr (SPLIT_P) split_bf16x8(p, p_hi[h], p_lo[h]);
+        else p_hi[h] = pack_bf16x8(p);
+        if constexpr (SPLIT_DS) split_bf16x8(ds, ds_hi[h], ds_lo[h]);
+        else ds_hi[h] = pack_bf16x8(ds);
+      };
+      // dV^T += dO^T P, dK^T += Q^T dS over half h's 32 queries
+      auto grad_products = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
         for (int db = 0; db < T::kDBlocks; ++db) {
           const int off = (16 * db + c16) * T::kTStride + 32 * h + 8 * (g ^ par23(c16));
           const u32x4_t ao = *reinterpret_cast<const u32x4_t*>(&sQOt[buf][1][off]);
           const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(&sQOt[buf][0][off]);
-          dv[db] = mfma_16x16x32_bf16(ao, p_hi, dv[db]);
-          if constexpr (SPLIT_P) dv[db] = mfma_16x16x32_bf16(ao, p_lo, dv[db]);
-          dk[db] = mfma_16x16x32_bf16(aq, ds_hi, dk[db]);
-          if constexpr (SPLIT_DS) dk[db] = mfma_16x16x32_bf16(aq, ds_lo, dk[db]);
+          dv[db] = mfma_16x16x32_bf16(ao, p_hi[h], dv[db]);
+          if constexpr (SPLIT_P) dv[db] = mfma_16x16x32_bf16(ao, p_lo[h], dv[db]);
+          dk[db] = mfma_16x16x32_bf16(aq, ds_hi[h], dk[db]);
+          if constexpr (SPLIT_DS) dk[db] = mfma_16x16x32_bf16(aq, ds_lo[h], dk[db]);
         }
-        sched_reads_ahead<2 * T::kDBlocks, (SPLIT_P || SPLIT_DS) ? 2 : 1>();
+      };
+      constexpr int kGradMfma = T::kDBlocks * (2 + SPLIT_P + SPLIT_DS);
+      // the row statistics of all 64 queries first: LDS reads complete in
+      // order, so a late read would hold up the weights behind operand reads
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const int ql = 32 * h + 16 * qq + 4 * g;
+          lq[h][qq] = *reinterpret_cast<const f32x4_t*>(&sL[buf][ql]);
+          dq4[h][qq] = *reinterpret_cast<const f32x4_t*>(&sD[buf][ql]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      sp_products(0);
+      sched_reads_ahead<4 * T::kKSteps, 1>();
+      sp_products(1);
+      weights(0);
+      sched_mix<4 * T::kKSteps, 4 * T::kKSteps, 2>();
+      grad_products(0);
+      weights(1);
+      sched_mix<2 * T::kDBlocks, kGradMfma, 2>();
+      grad_products(1);
+      sched_reads_ahead<2 * T::kDBlocks, (SPLIT_P || SPLIT_DS) ? 2 : 1>();
     };
     if (kw0 < N && !(CAUSAL && q0 + kQT - 1 < kw0)) {
       if ((q0 + kQT > N) || (kw0 + 16 > N) || (CAUSAL && q0 < kw0 + 15))
@@ -590,6 +644,11 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
         tile_body(std::false_type{});
     }
     __syncthreads();   // tile t+1 stored; everyone is done with buffer `buf`
+  };
+  // two iterations per trip, so that the register set of each is static
+  for (int t = 0; t < n_tiles; t += 2) {
+    iter(t, S1{});
+    if (t + 1 < n_tiles) iter(t + 1, S0{});
   }
 
   if (key < N) {

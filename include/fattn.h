@@ -40,10 +40,9 @@
  *                         to 16 bytes (4 for lse), an output overlapping an
  *                         input, sizes whose index space exceeds 2^62 or
  *                         whose row count B*H*N exceeds 2^31 - 1, or (the bf16
- *                         and fp8 forwards) one head's K or V slab of
+ *                         and fp8 forwards, the backward) one head's slab of
  *                         (N + 64) * d elements exceeding 2^31 - 1 bytes
- *                         (the last key tile addresses up to 64 rows past
- *                         N);
+ *                         (the last tile addresses up to 64 rows past N);
  *     FA_ERR_UNSUPPORTED  a head dimension other than 64 or 128;
  *     FA_ERR_HIP          the HIP runtime refused the launch;
  *     FA_ERR_TOO_LARGE    (fa_bwd_noalloc only) the problem exceeds its fixed

@@ -163,6 +163,12 @@ def test_backward_validation():
         assert bwd(**kw) == INV, kw
     assert bwd(d=80) == fa.FA_ERR_UNSUPPORTED
     assert bwd(N=0, q=None, dq=None) == fa.FA_OK
+    # dK/dV reads one head's Q and dO rows, up to 64 past N, through a 32-bit
+    # buffer range: (N + 64) * d * 2 bytes must stay below 2^31
+    for d in (128, 64):
+        n_max = (2 ** 31 - 1) // (2 * d) - 64
+        for n in (n_max + 1, (2 ** 31 - 1) // (2 * d)):
+            assert bwd(H=1, Hkv=1, N=n, d=d) == INV, (n, d)
 
 
 def test_backward_noalloc_validation():
@@ -185,6 +191,7 @@ def test_backward_noalloc_validation():
         assert nb(**kw) == INV, kw
     assert nb(d=80) == fa.FA_ERR_UNSUPPORTED
     assert nb(N=0, q=None, dq=None) == fa.FA_OK
+    assert nb(B=1, H=1, Hkv=1, N=(2 ** 31 - 1) // 256 - 63) == INV   # head slab over 2^31
     # the fixed scratch holds 2^22 rows of D: one row more is refused
     assert nb(B=1, H=1, Hkv=1, N=(1 << 22) + 1) == fa.FA_ERR_TOO_LARGE
     assert nb(B=2, H=32, Hkv=8, N=65537) == fa.FA_ERR_TOO_LARGE
