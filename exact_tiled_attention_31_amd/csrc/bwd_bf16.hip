@@ -26,8 +26,10 @@
 // The rows kernels take each 64-key tile as two 32-key halves, one after the
 // other, so only one half's scores, dP and dS are live: both then fit two
 // waves per SIMD (at most 256 registers per lane).
-// P and dS enter the matrix cores as hi + lo bf16 pairs (two steps against
-// the same exact bf16 operand), so their rounding stays near fp32.
+// dS enters the dQ product as one bf16 value.  In dK and dV, which sum over
+// every query head of a kv head, P and dS enter as hi + lo bf16 pairs (two
+// steps against the same exact bf16 operand) where the group size needs it,
+// so their rounding stays near fp32 (see the launch).
 #include <type_traits>
 
 #include "common.hpp"
@@ -212,14 +214,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
   constexpr int kVCopies = kKT * kVSlots / 64;         // wave-wide copies per tile
   static_assert((kKT * kVSlots) % 64 == 0, "whole copy instructions");
   u32x4_t kr[4];
+  // one head's K rows through a range-checked buffer: rows past N read as
+  // zero, byte offsets below 2^31 (checked at the API)
+  const i32x4_t k_rsrc = make_buffer_rsrc(K + head_kv * D, (uint32_t)N * D * 2);
   auto fetch = [&](int k0) {
     if (MODE == kGrad && loader) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kj = k0 + blk_r + r;
-        kr[r] = kj < N ? *reinterpret_cast<const u32x4_t*>(K + (head_kv + kj) * D + blk_c)
-                       : u32x4_t{0, 0, 0, 0};
-      }
+      for (int r = 0; r < 4; ++r) kr[r] = buffer_load_b128(k_rsrc, ((k0 + blk_r + r) * D + blk_c) * 2);
     }
   };
   auto copy_rows = [&](const uint16_t* __restrict__ src, uint16_t* dst, int k0) {
@@ -306,9 +307,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) ds[r] = pv[r] * (p_acc[r] - dd);
-        u32x4_t ds_hi[2], ds_lo[2];
+        // dS rounded once to bf16: no kv-head group sum here, and against
+        // the float64 definition dQ stays within 0.67 of the error bound
+        // (0.43 with a hi + lo pair, which costs 7% of the backward)
+        u32x4_t dsb[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) split_bf16x8(&ds[8 * t], ds_hi[t], ds_lo[t]);
+        for (int t = 0; t < 2; ++t) dsb[t] = pack_bf16x8(&ds[8 * t]);
         // dQ^T += K^T dS^T over this half's keys
 #pragma unroll
         for (int cb = 0; cb < T::kDBlocks; ++cb) {
@@ -316,11 +320,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
           for (int t = 0; t < 2; ++t) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
                 &sKt[buf][tr_read_off(T::kTStride, cb, col, kb, t, grp)]);
-            dq[cb] = mfma_32x32x16_bf16(a, ds_hi[t], dq[cb]);
-            dq[cb] = mfma_32x32x16_bf16(a, ds_lo[t], dq[cb]);
+            dq[cb] = mfma_32x32x16_bf16(a, dsb[t], dq[cb]);
           }
         }
-        sched_reads_ahead<2 * T::kDBlocks, 2, 2>();
+        sched_reads_ahead<2 * T::kDBlocks, 1>();
       }
     }
     };
