@@ -287,7 +287,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void fwd_fp8_kernel(
           for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sacc[kb][4 * w + i], c, -mref));
           sa += p[0] + p[2];
           sb += p[1] + p[3];
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          // the old-value operand only supplies bits 16..31, which the second
+          // conversion overwrites: any live register avoids a zero fill
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __builtin_bit_cast(int, p[0]), false);
           word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
           pf[4 * kb + w] = word;
         }
