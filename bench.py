@@ -17,7 +17,8 @@ stream before each step.  Prints one JSON line:
   roofline  the forward kernel against the dense bf16 matrix-core peak; its
             duration is the median of the per-step event times
   sclk      graphics clock sampled during the timed steps (SMU metrics), and
-            pct_clock_adjusted_peak = achieved / (peak * sclk / 2400 MHz)
+            pct_clock_adjusted_peak = achieved / (peak * sclk / 2400 MHz), or
+            null when the samples disagree by more than 10% (stale readings)
   flushed   median step time with a 512 MiB buffer written before each step
             (L2 and Infinity Cache cold)
   cpu_baseline  the float64 oracle on a bounded sample of the same inputs
@@ -492,9 +493,16 @@ def main():
         "sclk": sclk if sclk is not None else {"unavailable": clock.error},
     }
     if sclk is not None:
-        # the nominal peak assumes 2.4 GHz; the same work at the measured clock
-        adj_peak = PEAK_BF16_TFLOPS * sclk["mean_mhz"] / PEAK_SCLK_MHZ
-        out["pct_clock_adjusted_peak"] = round(100.0 * achieved / adj_peak, 2)
+        # the nominal peak assumes 2.4 GHz; the same work at the measured clock.
+        # The SMU table is refreshed by firmware and a short region can return
+        # stale readings (idle clocks from before the region): the adjusted
+        # figure is given only when the samples agree within 10%.
+        if sclk["samples"] >= 3 and sclk["min_mhz"] >= 0.9 * sclk["max_mhz"]:
+            adj_peak = PEAK_BF16_TFLOPS * sclk["mean_mhz"] / PEAK_SCLK_MHZ
+            out["pct_clock_adjusted_peak"] = round(100.0 * achieved / adj_peak, 2)
+        else:
+            out["pct_clock_adjusted_peak"] = None
+            sclk["note"] = "samples disagree by more than 10% (stale readings); not used"
     if args.flush_steps > 0:
         fl = flushed_steps(torch, call, stream, args.flush_steps, args.flush_mib * 2 ** 20)
         fm = median(fl)
