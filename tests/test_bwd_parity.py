@@ -74,6 +74,33 @@ def test_small_cases(case):
     compare(inp, dq, dk, dv, name)
 
 
+# dK/dV fetches its 64-query tiles three ahead into two register sets and runs
+# two iterations per loop trip: a key block's tile count (query heads of its
+# group x visible query tiles) sets which paths run.  Causal, one head per kv
+# head: the first key block sees N/64 tiles, 1 .. 5 here; two heads per kv
+# head non-causal: 2 * N/64 = 2 .. 10; three heads, ragged N: odd counts.
+TILE_COUNTS = [
+    ("mha_causal_N64", 1, 2, 2, 64, 128, True, 231),
+    ("mha_causal_N128", 1, 2, 2, 128, 128, True, 232),
+    ("mha_causal_N192", 1, 2, 2, 192, 128, True, 233),
+    ("mha_causal_N256", 1, 2, 2, 256, 128, True, 234),
+    ("mha_causal_N320", 1, 2, 2, 320, 128, True, 235),
+    ("gqa2_noncausal_N64", 1, 4, 2, 64, 128, False, 236),
+    ("gqa2_noncausal_N320", 1, 4, 2, 320, 128, False, 237),
+    ("gqa3_causal_N100_d64", 1, 6, 2, 100, 64, True, 238),
+    ("gqa3_noncausal_N190_d64", 1, 6, 2, 190, 64, False, 239),
+]
+
+
+@pytest.mark.parametrize("case", TILE_COUNTS, ids=[c[0] for c in TILE_COUNTS])
+def test_dkdv_tile_counts(case):
+    torch, fa = require_gpu()
+    name, B, H, Hkv, N, d, causal, seed = case
+    inp = W.gen_inputs(W.small_case(name, "bf16", B, H, Hkv, N, d, causal, seed, backward=True))
+    dq, dk, dv = run_fwd_bwd(inp, fa, torch)
+    compare(inp, dq, dk, dv, name)
+
+
 def test_c5_reduced_full():
     # C5's recipe (B=2, H=16, causal, dO iid N(0,1)) at N=512, every element.
     torch, fa = require_gpu()
