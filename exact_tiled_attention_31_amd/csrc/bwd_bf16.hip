@@ -554,8 +554,15 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
     const int hh = t / tiles_per_head;
     const int q0 = (qt_first + t - hh * tiles_per_head) * kQT;
     const int buf = t & 1;
-    if (t + 1 < n_tiles) stash(buf ^ 1, set_tag);   // that buffer was last read in iteration t-1
-    if (t + 3 < n_tiles) fetch(t + 3, set_tag);     // the set stash just emptied
+    // Staging of tile t+1 (into the other buffer, last read in iteration t-1)
+    // and the fetch of tile t+3 (into the register set the stash empties).
+    // Placed inside the tile, after the first half's dK, dV products: at the
+    // top of the tile, its LDS stores and the wait for its registers came
+    // before the first operand reads (measured 4% slower).
+    auto stage = [&]() __attribute__((always_inline)) {
+      if (t + 1 < n_tiles) stash(buf ^ 1, set_tag);
+      if (t + 3 < n_tiles) fetch(t + 3, set_tag);
+    };
     auto tile_body = [&](auto masked_tag) {
       constexpr bool need_mask = decltype(masked_tag)::value;
       // Two 32-query halves, software-pipelined inside the wave: the S, dP
@@ -637,6 +644,9 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
       grad_products(0);
       weights(1);
       sched_mix<2 * T::kDBlocks, kGradMfma, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+      stage();
+      __builtin_amdgcn_sched_barrier(0);
       grad_products(1);
       sched_reads_ahead<2 * T::kDBlocks, (SPLIT_P || SPLIT_DS) ? 2 : 1>();
     };
@@ -645,6 +655,8 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
         tile_body(std::true_type{});
       else
         tile_body(std::false_type{});
+    } else {
+      stage();
     }
     __syncthreads();   // tile t+1 stored; everyone is done with buffer `buf`
   };
