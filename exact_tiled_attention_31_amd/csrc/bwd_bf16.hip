@@ -503,9 +503,13 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
         rows[r] = buffer_load_b128(rs, ((q0 + blk_r + r) * D + blk_c) * 2);
     }
     if (tid < kQT) {
-      const int qi = q0 + tid;
-      lpre = qi < N ? LSE[head_q + qi] * kLog2e : 0.f;
-      dpre = qi < N ? delta[head_q + qi] : 0.f;
+      // raw values: a use here would wait for the loads at once (and hold up
+      // wave 0, and with it the barrier); they are scaled at the stash, two
+      // tiles later.  Rows past N read as zero (their weights are masked).
+      const i32x4_t l_rsrc = make_buffer_rsrc(LSE + head_q, (uint32_t)N * 4);
+      const i32x4_t d_rsrc = make_buffer_rsrc(delta + head_q, (uint32_t)N * 4);
+      lpre = buffer_load_f32(l_rsrc, (q0 + tid) * 4);
+      dpre = buffer_load_f32(d_rsrc, (q0 + tid) * 4);
     }
   };
   auto stash = [&](int buf, auto set_tag) {
@@ -536,7 +540,7 @@ __global__ __launch_bounds__(512, 1) void dk_dv16_kernel(
       }
     }
     if (tid < kQT) {
-      sL[buf][tid] = lpre;
+      sL[buf][tid] = lpre * kLog2e;
       sD[buf][tid] = dpre;
     }
   };

@@ -186,6 +186,15 @@ __device__ __forceinline__ u32x4_t buffer_load_b128(i32x4_t rsrc, int voffset) {
   return __builtin_bit_cast(u32x4_t, fattn_llvm_raw_buffer_load_v4i32(rsrc, voffset, 0, 0));
 }
 
+extern "C" __device__ float fattn_llvm_raw_buffer_load_f32(i32x4_t rsrc, int voffset, int soffset,
+                                                           int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.f32");
+
+// 4 bytes per lane from the buffer at byte `voffset` (zero past num_records).
+__device__ __forceinline__ float buffer_load_f32(i32x4_t rsrc, int voffset) {
+  return fattn_llvm_raw_buffer_load_f32(rsrc, voffset, 0, 0);
+}
+
 // Copy 16 bytes per lane from the buffer at `voffset` into LDS at
 // `lds_wave_dst + 16 * lane` (`lds_wave_dst` must be wave-uniform).
 __device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, void* lds_wave_dst, int voffset) {
