@@ -76,6 +76,22 @@ struct Tile8 {
   static_assert(kVPieces <= 64 * kWaves, "one V piece per thread at most");
 };
 
+// n matrix-core steps with two 16-byte operand reads each: the reads of the
+// first two steps first, then each step followed by the reads of the step
+// two ahead.
+template <int n>
+__device__ __forceinline__ void reads_ahead_fp8() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  constexpr int lead = n < 2 ? n : 2;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * lead, 0);
+#pragma unroll
+  for (int i = 0; i < n - lead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, lead, 0);
+}
+
 __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
   // formats 0/0 = e4m3 for A and B; block scales 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -242,13 +258,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void fwd_fp8_kernel(
       // S^T = K Q^T: two 32-key blocks, D/64 contraction steps each
       f32x16_t sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16_t{};
+      for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x16_t{};
+      // contraction step outermost: consecutive steps go to different
+      // accumulators; operand reads kept two steps ahead
 #pragma unroll
-        for (int s = 0; s < T::kKSteps; ++s)
+      for (int s = 0; s < T::kKSteps; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
           sacc[kb] = mfma_fp8(ld32(kt_lds + k_lane + 32 * kb * T::kKStride + 64 * s), qf[s],
                               sacc[kb]);
-      }
+      reads_ahead_fp8<2 * T::kKSteps>();
       if (msk) {
         asm volatile("" ::: "memory");   // a real branch: unmasked tiles pay nothing
 #pragma unroll
@@ -299,6 +318,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void fwd_fp8_kernel(
       for (int cb = 0; cb < T::kDBlocks; ++cb)
         oacc[cb] = mfma_fp8(ld32(vt_lds + vt_lane + 32 * cb * T::kVtStride + 128 * cb), pf,
                             oacc[cb]);
+      reads_ahead_fp8<T::kDBlocks>();
     }
 
     // tile kt+1 (K copy, V registers) must have landed; V^T goes into the
