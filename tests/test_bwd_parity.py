@@ -109,16 +109,17 @@ def test_c5_reduced_full():
     compare(inp, dq, dk, dv, "C5 N=512")
 
 
-def test_c5_full_size_sampled_heads():
-    # Full size; the oracle computes whole heads (all rows and keys) for a
-    # sample of (batch, head) pairs, compared element by element.
+def test_c5_full_size_all_heads():
+    # Full size (B=2, H=16, N=4096, d=128, causal), in the launch configuration
+    # the bench times: every element of dQ, dK and dV of all 32 heads against
+    # the float64 oracle (about 0.7 s of host time per head).
     torch, fa = require_gpu()
     w = W.C5
     inp = W.gen_inputs(w)
     dq, dk, dv = run_fwd_bwd(inp, fa, torch)
-    compare(inp, dq, dk, dv, "C5", heads=[(0, 0), (1, 7), (1, 15)])
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+    compare(inp, dq, dk, dv, "C5")
 
 
 def test_bwd_deterministic_bitwise():
