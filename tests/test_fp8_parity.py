@@ -148,34 +148,27 @@ def test_scales(scale):
 
 def test_f3_full_size():
     # C3's draws (32 query heads on 8 kv heads, N=8192, d=128, 1% of key rows
-    # x8) as e4m3 codes: two whole heads and 1024 sampled rows over all heads.
+    # x8) as e4m3 codes, in the launch configuration the bench times: every
+    # element of all 32 heads against the float64 oracle on the same codes
+    # (about 1.3 s of host time per head).
     torch, fa = require_gpu()
     w = W.F3
     inp = W.gen_inputs(w)
     o, lse = run_fp8(inp, fa, torch)
+    og, lg = dev_bf16_to_f64(o), dev_to_f64(lse)
     vsum_all = visible_abs_sums(inp, True)
-    for h in (0, w.H - 1):
+    worst_o, worst_l = 0.0, 0.0
+    for h in range(w.H):
         g = oracle.kv_head_of(h, w.H, w.Hkv)
         sl = (slice(None), slice(h, h + 1))
         qh, kh, vh = inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1]
         O, L = oracle.attention_fwd(qh, kh, vh, True, w.scale)
         PV, _ = oracle.attention_fwd(qh, kh, np.abs(vh), True, w.scale)
         e = head_score_error_bound(inp.q[0, h], inp.k[0, g], w.scale, True).reshape(1, 1, w.N)
-        check_fp8(dev_bf16_to_f64(o[sl]), O, PV, vsum_all[sl], f"F3 head {h}", e)
-        print(f"F3 head {h} lse max abs", check_lse8(dev_to_f64(lse[sl]), L, e, f"F3 head {h}"),
-              flush=True)
-    rng = np.random.default_rng(35)
-    hi = W.sample_rows(rng, w.H, w.N, 1024)
-    rows = np.concatenate([np.zeros((len(hi), 1), np.int64), hi], axis=1)
-    Or, Lr = oracle.attention_rows(inp.q, inp.k, inp.v, True, w.scale, rows)
-    PVr, _ = oracle.attention_rows(inp.q, inp.k, np.abs(inp.v), True, w.scale, rows)
-    og = dev_bf16_to_f64(o)
-    L = dev_to_f64(lse)
-    got = np.stack([og[b, h, i] for b, h, i in rows])
-    vs = np.stack([vsum_all[b, h, i] for b, h, i in rows])
-    e = score_error_bound(inp, w.scale, True, rows)
-    check_fp8(got, Or, PVr, vs, "F3 sampled rows", e)
-    check_lse8(np.array([L[b, h, i] for b, h, i in rows]), Lr, e, "F3 sampled rows")
+        info = check_fp8(og[sl], O, PV, vsum_all[sl], f"F3 head {h}", e)
+        worst_o = max(worst_o, info["max_abs"])
+        worst_l = max(worst_l, check_lse8(lg[sl], L, e, f"F3 head {h}"))
+    print(f"F3 all heads: O max abs {worst_o:.4g}, LSE max abs {worst_l:.3g}", flush=True)
 
 
 def test_deterministic_and_accepts_float8_dtype():
