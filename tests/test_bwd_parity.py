@@ -122,6 +122,26 @@ def test_c5_full_size_all_heads():
     compare(inp, dq, dk, dv, "C5")
 
 
+# Full-size shapes that take the other dK/dV instances and the non-causal
+# kernels: every element of every head against the float64 oracle.
+FULL = [
+    # name, B, H, Hkv, N, d, causal, seed
+    ("gqa4_causal_N4096", 1, 32, 8, 4096, 128, True, 241),    # hi + lo P and dS in dK/dV
+    ("gqa2_causal_N4096", 1, 16, 8, 4096, 128, True, 242),    # hi + lo P in dK/dV
+    ("mha_noncausal_N4096", 1, 8, 8, 4096, 128, False, 243),
+]
+
+
+@pytest.mark.parametrize("case", FULL, ids=[c[0] for c in FULL])
+def test_full_size_shapes(case):
+    name, B, H, Hkv, N, d, causal, seed = case
+    torch, fa = require_gpu()
+    w = W.C5.with_(name=name, B=B, H=H, Hkv=Hkv, N=N, d=d, causal=causal, seed=seed)
+    inp = W.gen_inputs(w)
+    dq, dk, dv = run_fwd_bwd(inp, fa, torch)
+    compare(inp, dq, dk, dv, name)
+
+
 def test_bwd_deterministic_bitwise():
     torch, fa = require_gpu()
     inp = W.gen_inputs(W.C5.with_(N=1024, B=1, H=4, Hkv=2))
