@@ -69,30 +69,25 @@ def test_window_covering_sequence_equals_causal_forward_bitwise():
 
 def test_c3_shape_window_256_with_outliers():
     # The headline shape (32 query heads on 8 kv heads, N=8192, d=128, 1% of
-    # key rows x8) with the pages' window of 256: two whole heads element by
-    # element and 1024 sampled rows over all heads.
+    # key rows x8) with the pages' window of 256, in the launch configuration
+    # the bench times: every element of all 32 heads against the float64
+    # oracle's window variant (about 0.2 s of host time per head).
     torch, fa = require_gpu()
     w = W.C3
     window = 256
     inp = W.gen_inputs(w)
     o, lse = run_local(inp, fa, torch, window)
-    for h in (0, w.H - 1):
+    og, lg = dev_bf16_to_f64(o), dev_to_f64(lse)
+    worst_o, worst_l = 0.0, 0.0
+    for h in range(w.H):
         g = oracle.kv_head_of(h, w.H, w.Hkv)
         O, L = oracle.attention_fwd(inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1],
                                     True, w.scale, window=window)
-        check_bf16(dev_bf16_to_f64(o[:, h:h + 1]), O, f"C3 local head {h}")
-        check_lse(dev_to_f64(lse[:, h:h + 1]), L, f"C3 local head {h}")
-    rng = np.random.default_rng(34)
-    hi = W.sample_rows(rng, w.H, w.N, 1024)
-    rows = np.concatenate([np.zeros((len(hi), 1), np.int64), hi], axis=1)
-    Or, Lr = oracle.attention_rows(inp.q, inp.k, inp.v, True, w.scale, rows, window=window)
-    ob = dev_bf16_bits(o)
-    L = dev_to_f64(lse)
-    got = np.stack([W.bf16_bits_to_f32(ob[b, h, i]) for b, h, i in rows]).astype(np.float64)
-    info = check_bf16(got, Or, "C3 local sampled rows")
-    info["lse_max_abs"] = check_lse(np.array([L[b, h, i] for b, h, i in rows]), Lr,
-                                    "C3 local sampled rows")
-    print("C3 local w=256", info, flush=True)
+        info = check_bf16(og[:, h:h + 1], O, f"C3 local head {h}")
+        worst_o = max(worst_o, info["max_abs"])
+        worst_l = max(worst_l, check_lse(lg[:, h:h + 1], L, f"C3 local head {h}"))
+    print(f"C3 local w=256, all heads: O max abs {worst_o:.4g}, LSE max abs {worst_l:.3g}",
+          flush=True)
 
 
 def test_deterministic():
