@@ -164,6 +164,15 @@ def test_c4_full_size_sampled_rows_prefix_and_workspace():
     rows = np.concatenate([np.zeros((len(inp.sampled_rows), 1), np.int64), inp.sampled_rows], axis=1)
     _compare_rows(inp, o, lse, rows, "C4 sampled rows")
     _lse_bounds(inp, lse, "C4")
+    # one whole head per kv head, every row and column (a few seconds of host
+    # time per head for the float64 oracle at this length on a 16-core host)
+    for h in range(w.H // w.Hkv - 1, w.H, w.H // w.Hkv):
+        g = oracle.kv_head_of(h, w.H, w.Hkv)
+        O, L = oracle.attention_fwd(inp.q[:, h:h + 1], inp.k[:, g:g + 1], inp.v[:, g:g + 1],
+                                    True, w.scale)
+        info = check_bf16(dev_bf16_to_f64(o[:, h:h + 1]), O, f"C4 head {h}")
+        info["lse_max_abs"] = check_lse(dev_to_f64(lse[:, h:h + 1]), L, f"C4 head {h}")
+        print(f"C4 head {h}", info, flush=True)
 
     # Prefix consistency: causal rows i < 8192 see only keys < 8192, so a run
     # on the truncated inputs must give the same rows (same tile order: bitwise).
