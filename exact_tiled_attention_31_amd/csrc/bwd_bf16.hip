@@ -207,9 +207,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
   // needs no transposed K): tile kt+1 is copied global -> LDS by the load unit
   // at the start of iteration kt, straight into the padded (and, for dQ,
   // swizzled) layout: each 16-byte slot fetches the chunk that belongs there.
-  // Both overlap tile kt's compute; one barrier per tile.  Rows past N are
-  // zero for K in registers and a copy of row N-1 when copied (finite, and
-  // their weights are exactly 0).
+  // Both overlap tile kt's compute; one barrier per tile.  The D pass's copies
+  // go through range-checked buffers (one 32-bit offset per copy; rows past N
+  // read as zero); dQ's V copies use per-lane addresses with rows past N
+  // clamped to row N-1 (its registers are at the limit, and the buffer form
+  // spills there).  Rows past N are zero for K in registers.  All of them are
+  // finite and their weights are exactly 0.
   constexpr int kVSlots = T::kRowStride / 8;           // 16-byte slots per LDS row
   constexpr int kVCopies = kKT * kVSlots / 64;         // wave-wide copies per tile
   static_assert((kKT * kVSlots) % 64 == 0, "whole copy instructions");
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
       for (int r = 0; r < 4; ++r) kr[r] = buffer_load_b128(k_rsrc, ((k0 + blk_r + r) * D + blk_c) * 2);
     }
   };
-  auto copy_rows = [&](const uint16_t* __restrict__ src, uint16_t* dst, int k0) {
+  const i32x4_t v_rsrc = make_buffer_rsrc(V + head_kv * D, (uint32_t)N * D * 2);
+  auto copy_rows = [&](const uint16_t* __restrict__ src, i32x4_t rsrc, uint16_t* dst, int k0) {
 #pragma unroll
     for (int j0 = 0; j0 < kVCopies; j0 += WAVES) {
       const int j = j0 + wave;
@@ -233,16 +237,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void rows_kernel(
         const int slot = slot_all - row * kVSlots;
         if (slot < D / 8) {
           const int chunk = kSwz ? slot ^ rm_swz(row) : slot;
-          const int kj = min(k0 + row, N - 1);
-          global_load_lds16(src + (head_kv + kj) * D + 8 * chunk, dst + 512 * j);
+          if constexpr (MODE == kDelta) {
+            buffer_load_lds16(rsrc, dst + 512 * j, ((k0 + row) * D + 8 * chunk) * 2);
+          } else {
+            const int kj = min(k0 + row, N - 1);
+            global_load_lds16(src + (head_kv + kj) * D + 8 * chunk, dst + 512 * j);
+          }
         }
       }
     }
   };
   // the D pass has no transposed K tile: K is copied by the load unit as V is
   auto copy_v = [&](int k0, int buf) {
-    copy_rows(V, sV[buf], k0);
-    if constexpr (MODE == kDelta) copy_rows(K, sK[buf], k0);
+    copy_rows(V, v_rsrc, sV[buf], k0);
+    if constexpr (MODE == kDelta) copy_rows(K, k_rsrc, sK[buf], k0);
   };
   auto stash = [&](int buf) {
     if (MODE == kGrad && loader) {
