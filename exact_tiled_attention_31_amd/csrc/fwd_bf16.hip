@@ -188,16 +188,24 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fwd_bf16_kernel(
     const int chunk = slot - row * slots_per_row;
     return chunk < T::kChunks ? row * T::kRowBytes + 16 * chunk : -1;
   };
+  // Per-lane offsets of this wave's copy slots within a tile, fixed for the
+  // whole loop; pad slots get 2^31, which with any tile base below 2^31 lands
+  // past the buffer's range and reads as zero (no per-copy select).
+  constexpr int kKCopiesPerWave = (T::kKCopies + kSplitWaves - 1) / kSplitWaves;
+  uint32_t k_off[kKCopiesPerWave];
+#pragma unroll
+  for (int i = 0; i < kKCopiesPerWave; ++i) {
+    const int off = copy_offset(64 * (kSplitWaves * i + wl) + lane, T::kKSlots);
+    k_off[i] = off < 0 ? 0x80000000u : (uint32_t)off;
+  }
   auto issue_k_tile = [&](int k0, int buf) {
     uint8_t* kdst = smem + buf * kStage;
-    const int base = k0 * T::kRowBytes;
+    const uint32_t base = (uint32_t)k0 * T::kRowBytes;
 #pragma unroll
-    for (int j0 = 0; j0 < T::kKCopies; j0 += kSplitWaves) {
-      const int j = j0 + wl;
-      if (j < T::kKCopies) {
-        const int off = copy_offset(64 * j + lane, T::kKSlots);
-        buffer_load_lds16(k_rsrc, kdst + 1024 * j, off < 0 ? (int)kv_bytes : base + off);
-      }
+    for (int i = 0; i < kKCopiesPerWave; ++i) {
+      const int j = kSplitWaves * i + wl;
+      if (j < T::kKCopies)
+        buffer_load_lds16(k_rsrc, kdst + 1024 * j, (int)(base + k_off[i]));
     }
   };
   // V goes through registers so it can be stored transposed: thread = (4-key
