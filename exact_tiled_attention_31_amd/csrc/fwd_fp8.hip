@@ -166,20 +166,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void fwd_fp8_kernel(
   if (CAUSAL) n_kt = min(n_kt, (q_hi - 1) / kBN + 1);
 
   // ---- K tile copy: wave-wide instruction j fills LDS slots 64j .. 64j+63 ---
-  const uint32_t kv_bytes = (uint32_t)N * T::kRowBytes;
+  // Per-lane offsets of this wave's copy slots within a tile, fixed for the
+  // whole loop; pad slots get 2^31, which with any tile base below 2^31 lands
+  // past the buffer's range and reads as zero (no per-copy select).
+  constexpr int kKCopiesPerWave = (T::kKCopies + kWaves - 1) / kWaves;
+  uint32_t k_off[kKCopiesPerWave];
+#pragma unroll
+  for (int i = 0; i < kKCopiesPerWave; ++i) {
+    const int slot = 64 * (kWaves * i + wave) + lane;
+    const int row = slot / T::kKSlots;
+    const int chunk = slot - row * T::kKSlots;
+    k_off[i] = chunk < T::kChunks ? (uint32_t)(row * T::kRowBytes + 16 * chunk) : 0x80000000u;
+  }
   auto issue_k_tile = [&](int k0, int buf) {
     uint8_t* kdst = smem + buf * T::kStage;
-    const int base = k0 * T::kRowBytes;
+    const uint32_t base = (uint32_t)k0 * T::kRowBytes;
 #pragma unroll
-    for (int j0 = 0; j0 < T::kKCopies; j0 += kWaves) {
-      const int j = j0 + wave;
-      if (j < T::kKCopies) {
-        const int slot = 64 * j + lane;
-        const int row = slot / T::kKSlots;
-        const int chunk = slot - row * T::kKSlots;
-        const int off = chunk < T::kChunks ? base + row * T::kRowBytes + 16 * chunk : (int)kv_bytes;
-        buffer_load_lds16(k_rsrc, kdst + 1024 * j, off);
-      }
+    for (int i = 0; i < kKCopiesPerWave; ++i) {
+      const int j = kWaves * i + wave;
+      if (j < T::kKCopies) buffer_load_lds16(k_rsrc, kdst + 1024 * j, (int)(base + k_off[i]));
     }
   };
   // ---- V tile: thread = (4-key group, 8-column chunk) loads 4 x 8 bytes and
